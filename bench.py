@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM on one MI355X.
+
+Workload (default): C[16384,16384] = A[16384,4096] @ B[4096,16384], fp16 inputs
+drawn uniformly from [-1, 1) with a fixed seed, fp32 accumulation, fp16 output.
+A step is one GEMM launch over device-resident inputs.  Prints one JSON line:
+throughput (TFLOP/s = 2MNK / t), the roofline of the kernel (achieved vs MI355X
+dense fp16 MFMA peak, from HIP events on the launch stream), the HBM traffic the
+last hardware-counter profile measured for this kernel source, and the CPU
+oracle's throughput on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME] [--sweep]
+
+Schedules are written order[+remap]/mode[/P<programs>][/tile], e.g.
+"grouped8+remap/tiled", "rowmajor/persistent/P256", "grouped8/crosstile".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
+METRIC = "fp16 GEMM TFLOPS (2MNK/s) + % MFMA peak at M=N=16384, K=4096"
+DEFAULT_SCHEDULE = "grouped8+remap/tiled"
+KERNEL_SOURCES = ["tile_scheduling_amd/csrc/gemm_kernel.hpp", "tile_scheduling_amd/csrc/schedule.hpp",
+                  "tile_scheduling_amd/csrc/internal.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_schedule(text: str):
+    import tile_scheduling_amd as ts
+
+    parts = text.split("/")
+    order_s = parts[0]
+    remap = order_s.endswith("+remap")
+    order_s = order_s.replace("+remap", "")
+    if order_s in ("rowmajor", "row_major"):
+        order, G = "row_major", 8
+    else:
+        m = re.fullmatch(r"grouped(\d+)", order_s)
+        if not m:
+            raise ValueError(f"bad order {order_s!r}")
+        order, G = "grouped", int(m.group(1))
+    mode = parts[1] if len(parts) > 1 else "tiled"
+    P, tile = 0, "auto"
+    for extra in parts[2:]:
+        if extra.startswith("P"):
+            P = int(extra[1:])
+        else:
+            tile = extra
+    return ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, sched_label: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_0-9]+):\s*(\S+)\s*$", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("source_sha") != sources_sha() or vals.get("schedule") != sched_label:
+        return None
+    try:
+        return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def time_gemm(ts, torch, a, b, c, sched, steps, warmup):
+    for _ in range(warmup):
+        ts.gemm(a, b, out=c, schedule=sched)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        ts.gemm(a, b, out=c, schedule=sched)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return {"wall_s": wall, "event_ms": ev[0].elapsed_time(ev[-1]) / steps, "median_ms": per[len(per) // 2],
+            "min_ms": per[0], "max_ms": per[-1]}
+
+
+def cpu_baseline(A, B, w, budget_s: float):
+    """The oracle on whole rows of C, sized to about budget_s seconds of host work."""
+    from oracle import gemm as og
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = threads
+    t0 = time.perf_counter()
+    og.gemm(A, B, w.ab_dtype, rows=(0, rows), threads=threads)
+    t_cal = time.perf_counter() - t0
+    rows = int(min(w.M, max(threads, threads * round(budget_s / max(t_cal, 1e-6)))))
+    t0 = time.perf_counter()
+    og.gemm(A, B, w.ab_dtype, rows=(0, rows), threads=threads)
+    t = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * w.N * w.K / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} full rows of C ({rows}x{w.N} outputs, K={w.K}, fp64 accumulation) "
+                      f"in {t:.1f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gemm_16384x16384x4096_f16")
+    ap.add_argument("--schedule", default=DEFAULT_SCHEDULE)
+    ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMM is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tile_scheduling_amd as ts
+    import workloads
+
+    by_name = {w.name: w for w in workloads.ALL}
+    w = by_name[args.workload]
+    out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.c_dtype]
+    in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
+
+    A, B = workloads.inputs(w)
+    a = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
+    b = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
+    c = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
+    flops = 2.0 * w.M * w.N * w.K
+
+    if args.sweep:
+        labels = []
+        for order in ("rowmajor", "grouped4", "grouped8", "grouped16"):
+            for remap in ("", "+remap"):
+                for mode in ("tiled", "persistent", "crosstile"):
+                    labels.append(f"{order}{remap}/{mode}")
+        for lab in labels:
+            s = parse_schedule(lab)
+            r = time_gemm(ts, torch, a, b, c, s, max(5, args.steps // 2), 2)
+            log(f"sweep {w.name} {lab:28s} median {r['median_ms']:.4f} ms  "
+                f"{flops / r['median_ms'] / 1e9:9.1f} TFLOP/s")
+
+    sched = parse_schedule(args.schedule)
+    q = ts.query(w.M, w.N, w.K, sched, ts.TS_F16 if w.ab_dtype == "f16" else ts.TS_BF16,
+                 {"f16": ts.TS_F16, "bf16": ts.TS_BF16, "f32": ts.TS_F32}[w.c_dtype])
+    log(f"launch {sched.label()}: {q}")
+    r = time_gemm(ts, torch, a, b, c, sched, args.steps, args.warmup)
+    ms_per_step = r["wall_s"] * 1e3 / args.steps
+    value = flops * args.steps / r["wall_s"] / 1e12
+    achieved = flops / (r["event_ms"] * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: wall {ms_per_step:.4f} ms/step, events {r['event_ms']:.4f} ms/launch "
+        f"(median {r['median_ms']:.4f}, min {r['min_ms']:.4f}, max {r['max_ms']:.4f})")
+
+    traffic = measured_traffic(w.name, sched.label())
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.ab_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.ab_dtype, "acc": "f32",
+                   "out": w.c_dtype, "inputs": f"{w.dist} seed {w.seed}", "schedule": sched.label(),
+                   "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "grid": q["grid"]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(A, B, w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * tsgemm -- tiled dense matrix multiply with tile-order schedules, for AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (from "Week-4 notes: Roofline and Tiling", section 1, and the
+ * naive tiled matmul listing of "(1/n) Triton matmul ... persistent kernel"):
+ *
+ *     C[M,N] = A[M,K] @ B[K,N]       C[i][j] = sum_k A[i][k] * B[k][j]
+ *
+ * with fp16 or bf16 inputs, an fp32 accumulator held on chip for the whole K
+ * loop, and one conversion of the accumulator to the output type (round to
+ * nearest even) when the output tile is stored.  The output C is split into
+ * BLOCK_M x BLOCK_N tiles; the schedule decides which workgroup computes which
+ * tile and in what order (see ts_schedule below).
+ *
+ * Conventions shared by every entry point
+ *   - Matrix pointers are DEVICE pointers, owned by the caller; the library never
+ *     frees them and keeps no reference after the call is enqueued.
+ *   - Strides are in ELEMENTS, as in the pages' kernels: element (i,k) of A is
+ *     A[i*stride_am + k*stride_ak], (k,j) of B is B[k*stride_bk + j*stride_bn],
+ *     (i,j) of C is C[i*stride_cm + j*stride_cn].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without synchronising.
+ *   - Arguments are validated on the host before any HIP call; an invalid call
+ *     returns an error code and enqueues nothing.  No entry point allocates
+ *     device memory.
+ *   - Thread-safe: the only state is a per-device cache of device properties.
+ */
+#ifndef TSGEMM_H
+#define TSGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TS_OK = 0,
+    TS_ERR_INVALID_ARG = -1,  /* null pointer with work to do, negative size, bad stride, bad schedule */
+    TS_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement (dtype pair, stride pattern) */
+    TS_ERR_ALIGNMENT = -3,    /* a pointer is not aligned to its element size */
+    TS_ERR_HIP = -4,          /* the HIP runtime reported an error (query or launch) */
+    TS_ERR_NO_DEVICE = -5     /* the request needs a GPU and none is usable */
+} ts_status;
+
+/* element types */
+enum { TS_F16 = 1, TS_BF16 = 2, TS_F32 = 3 };
+
+/* tile order: which output tile a linear tile id denotes */
+enum {
+    /* tile_m = id / num_n_tiles, tile_n = id % num_n_tiles
+       ("(1/n) ... persistent kernel", naive tiled matmul listing) */
+    TS_ORDER_ROW_MAJOR = 0,
+    /* grouped ordering / CTA swizzle: ids walk GROUP_SIZE_M tile rows at a time,
+       M coordinate first; the last group holds the remaining num_m_tiles mod G
+       rows ("(2/n) ... grouped ordering (CTA swizzle)", section Implementation) */
+    TS_ORDER_GROUPED = 1
+};
+
+/* how workgroups take tiles */
+enum {
+    /* one workgroup per tile; the hardware dispatcher assigns them */
+    TS_MODE_TILED = 0,
+    /* P = min(num_programs, num_tiles) workgroups; workgroup p computes tile ids
+       p, p+P, p+2P, ... ("(1/n) ...", naive persistent listing and grid code) */
+    TS_MODE_PERSISTENT = 1,
+    /* as PERSISTENT, but the tile loop and the K loop are one flattened loop, so
+       the next tile's first K slices are fetched while the current tile is being
+       stored ("(3/n) ... cross tile pipelining", merged loop) */
+    TS_MODE_CROSSTILE = 2
+};
+
+/* tile configurations (BLOCK_M x BLOCK_N x BLOCK_K) */
+enum {
+    TS_TILE_AUTO = 0,          /* library chooses from the shape */
+    TS_TILE_64x64x32 = 1,
+    TS_TILE_128x128x64 = 2,
+    TS_TILE_256x256x64 = 3
+};
+
+typedef struct {
+    int32_t order;         /* TS_ORDER_*                                                      */
+    int32_t group_m;       /* GROUP_SIZE_M >= 1, read when order == TS_ORDER_GROUPED; values
+                              above num_m_tiles act as num_m_tiles (column-major order)       */
+    int32_t mode;          /* TS_MODE_*                                                       */
+    int32_t num_programs;  /* persistent modes: workgroups to launch; 0 = number of CUs times
+                              the workgroups one CU holds for the chosen kernel; always capped
+                              at num_tiles.  Ignored for TS_MODE_TILED.                        */
+    int32_t xcd_remap;     /* 1 = renumber workgroups so that each XCD (chiplet with its own
+                              L2) works on one contiguous run of tile ids; 0 = off             */
+    int32_t tile_config;   /* TS_TILE_*                                                       */
+} ts_schedule;
+
+typedef struct {
+    int32_t block_m, block_n, block_k;  /* tile shape used                                   */
+    int32_t threads;                    /* threads per workgroup                             */
+    int64_t num_m_tiles, num_n_tiles;   /* cdiv(M, block_m), cdiv(N, block_n)                 */
+    int64_t k_steps;                    /* cdiv(K, block_k)                                   */
+    int64_t num_tiles;                  /* num_m_tiles * num_n_tiles                          */
+    int64_t grid;                       /* workgroups launched                                */
+    int32_t programs_per_cu;            /* workgroups one CU holds (0 if no device)           */
+    int32_t cu_count;                   /* compute units of the current device (0 if none)    */
+    int32_t xcds;                       /* XCDs the workgroups are dealt over (8 if no device) */
+    int32_t lds_bytes;                  /* LDS per workgroup                                   */
+    int32_t masked;                     /* 1 = edge-masked kernel variant (ragged or unaligned) */
+    int32_t vgprs;                      /* registers per thread reported by the runtime (-1 if none) */
+    int32_t scratch_bytes;              /* private (spill) bytes per thread (-1 if none)       */
+} ts_launch_info;
+
+/*
+ * C = A @ B on `stream`.
+ *   A: M x K, B: K x N, C: M x N, strides as above.  Supported: stride_ak ==
+ *   stride_bn == stride_cn == 1 (row-major, as the pages' fp16 runs use); any
+ *   other inner stride returns TS_ERR_UNSUPPORTED.  Row strides must satisfy
+ *   stride_am >= K, stride_bk >= N, stride_cm >= N (when there is more than one row).
+ *   ab_dtype / c_dtype: TS_F16 -> TS_F16 or TS_F32; TS_BF16 -> TS_BF16 or TS_F32.
+ *   M == 0 or N == 0: nothing to do, TS_OK.  K == 0: C is set to zero.
+ *   Ragged M, N, K and row strides that defeat 16-byte vector access are handled
+ *   by masked loads and stores (out-of-range A and B elements read as zero; C is
+ *   written only inside M x N).  sched == NULL means row-major tiled, auto tile.
+ *   The result does not depend on the schedule: every schedule with the same tile
+ *   configuration produces bit-identical C.
+ *   Errors: TS_ERR_INVALID_ARG / TS_ERR_UNSUPPORTED / TS_ERR_ALIGNMENT before any
+ *   HIP call; TS_ERR_NO_DEVICE if no GPU; TS_ERR_HIP if the launch fails.
+ */
+ts_status ts_gemm(const void* A, const void* B, void* C,
+                  int64_t M, int64_t N, int64_t K,
+                  int64_t stride_am, int64_t stride_ak,
+                  int64_t stride_bk, int64_t stride_bn,
+                  int64_t stride_cm, int64_t stride_cn,
+                  int32_t ab_dtype, int32_t c_dtype,
+                  const ts_schedule* sched, void* stream);
+
+/*
+ * Writes the work sequence of every workgroup, computed on the GPU by the same
+ * device functions the GEMM kernels use, to the device buffer `out` of
+ * out_rows x 5 int32: row (p * max_items + it) = (p, it, tile_m, tile_n, k_step)
+ * for the it-th (tile, K-step) item workgroup p processes, where max_items =
+ * cdiv(num_tiles, grid) * max(k_steps, 1); rows past a workgroup's item count are
+ * filled with -1.  out_rows must be >= grid * max_items (see ts_query).
+ * Same validation and error codes as ts_gemm (no matrix pointers involved).
+ */
+ts_status ts_schedule_trace(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                            const ts_schedule* sched, int32_t* out, int64_t out_rows, void* stream);
+
+/*
+ * Host-side twin of ts_schedule_trace: the same schedule functions run on the
+ * CPU into the host buffer `out`.  `cu_count` and `programs_per_cu` stand in for
+ * the device when sched->num_programs == 0 in a persistent mode.  No HIP call.
+ */
+ts_status ts_schedule_trace_host(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                                 const ts_schedule* sched, int32_t cu_count, int32_t programs_per_cu,
+                                 int32_t* out, int64_t out_rows);
+
+/*
+ * Fills `out` with the launch ts_gemm would make for these arguments (tile
+ * shape, tile counts, grid, occupancy, registers).  Needs a device only when the
+ * grid depends on it (persistent mode with num_programs == 0) or for the
+ * occupancy and register fields, which are 0 / -1 without one.
+ */
+ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                   const ts_schedule* sched, ts_launch_info* out);
+
+/* Static, human-readable name of a status code. */
+const char* ts_status_string(ts_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSGEMM_H */

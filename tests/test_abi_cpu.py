@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: loads, exports every declared symbol, validates
+arguments before any HIP call, and its host-side schedule equals the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import tile_scheduling_amd as ts
+from oracle import schedule as osch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tsgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_symbols()
+    assert set(names) == set(ts.EXPORTS)
+    lib = ctypes.CDLL(ts.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert ts.status_string(code).startswith("TS_")
+    assert "unknown" in ts.status_string(17)
+
+
+# ---- validation happens before any HIP call (fake pointers are never touched) ------
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below is rejected first
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(M=-1), ts.TS_ERR_INVALID_ARG),
+    (dict(K=-5), ts.TS_ERR_INVALID_ARG),
+    (dict(ab=ts.TS_F16, c=ts.TS_BF16), ts.TS_ERR_UNSUPPORTED),
+    (dict(ab=ts.TS_F32, c=ts.TS_F32), ts.TS_ERR_UNSUPPORTED),
+    (dict(ab=9), ts.TS_ERR_INVALID_ARG),
+    (dict(strides=(64, 2, 64, 1, 64, 1)), ts.TS_ERR_UNSUPPORTED),
+    (dict(strides=(64, 1, 64, 1, 64, 3)), ts.TS_ERR_UNSUPPORTED),
+    (dict(strides=(10, 1, 64, 1, 64, 1)), ts.TS_ERR_INVALID_ARG),   # lda < K
+    (dict(strides=(64, 1, 64, 1, 10, 1)), ts.TS_ERR_INVALID_ARG),   # ldc < N
+    (dict(a=FAKE + 1), ts.TS_ERR_ALIGNMENT),
+    (dict(c=ts.TS_F32, cptr=FAKE + 2), ts.TS_ERR_ALIGNMENT),
+    (dict(cptr=0), ts.TS_ERR_INVALID_ARG),
+    (dict(a=0), ts.TS_ERR_INVALID_ARG),
+    (dict(sched=ts.Schedule(order="grouped", group_m=0)), ts.TS_ERR_INVALID_ARG),
+    (dict(sched=ts.Schedule(mode="persistent", num_programs=-3)), ts.TS_ERR_INVALID_ARG),
+])
+def test_invalid_arguments_are_rejected(kw, expect):
+    M, N, K = kw.get("M", 64), 64, kw.get("K", 64)
+    st = ts.gemm_raw(kw.get("a", FAKE), FAKE, kw.get("cptr", FAKE), M, N, K,
+                     strides=kw.get("strides", (64, 1, 64, 1, 64, 1)),
+                     ab_dtype=kw.get("ab", ts.TS_F16), c_dtype=kw.get("c", ts.TS_F16),
+                     schedule=kw.get("sched"))
+    assert st == expect, ts.status_string(st)
+
+
+def test_bad_schedule_enums_are_rejected():
+    s = ts._Schedule(5, 1, 0, 0, 0, 0)
+    assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(s), None) == -1
+    for bad in (ts._Schedule(0, 1, 3, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9)):
+        assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(bad), None) == -1
+
+
+def test_empty_output_is_a_no_op():
+    assert ts.gemm_raw(0, 0, 0, 0, 64, 64) == ts.TS_OK
+    assert ts.gemm_raw(0, 0, 0, 64, 0, 64) == ts.TS_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_gpu_reports_no_device():
+    assert ts.gemm_raw(FAKE, FAKE, FAKE, 64, 64, 64) == ts.TS_ERR_NO_DEVICE
+
+
+# ---- launch planning ---------------------------------------------------------------
+
+def test_query_tile_grid_and_masking():
+    q = ts.query(256, 256, 256, ts.Schedule(tile="64x64x32"), ts.TS_F16, ts.TS_F32)
+    assert (q["block_m"], q["block_n"], q["block_k"]) == (64, 64, 32)
+    assert (q["num_m_tiles"], q["num_n_tiles"], q["k_steps"], q["grid"], q["masked"]) == (4, 4, 8, 16, 0)
+    q = ts.query(5000, 12290, 1000, ts.Schedule(mode="persistent", num_programs=256, tile="256x256x64"),
+                 ts.TS_BF16, ts.TS_F32)
+    assert (q["num_m_tiles"], q["num_n_tiles"], q["k_steps"]) == (20, 49, 16)
+    assert q["grid"] == 256 and q["masked"] == 1
+    q = ts.query(16384, 16384, 4096, ts.Schedule())
+    assert (q["block_m"], q["num_tiles"], q["masked"]) == (256, 4096, 0)
+    q = ts.query(64, 64, 0, ts.Schedule(mode="crosstile", num_programs=8))
+    assert q["k_steps"] == 0 and q["masked"] == 1  # K = 0 still writes C (zeros)
+
+
+# ---- host-side schedule (the same functions the kernels run) vs the oracle ----------
+
+def _oracle_sched(s: ts.Schedule, grid_programs):
+    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE}[s.mode]
+    order = osch.GROUPED if s.order == "grouped" else osch.ROW_MAJOR
+    return osch.Schedule(order=order, group_m=s.group_m, mode=mode, num_programs=grid_programs,
+                         xcd_remap=s.xcd_remap)
+
+
+CASES = [
+    (256, 256, 256, "64x64x32"),
+    (300, 520, 200, "64x64x32"),
+    (1000, 700, 96, "128x128x64"),
+    (5000, 12290, 1000, "256x256x64"),
+    (2048, 3072, 0, "256x256x64"),
+    (64, 64, 33, "64x64x32"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,tile", CASES)
+@pytest.mark.parametrize("order,G", [("row_major", 1), ("grouped", 3), ("grouped", 8), ("grouped", 100)])
+@pytest.mark.parametrize("mode,P", [("tiled", 0), ("persistent", 7), ("persistent", 256), ("crosstile", 256)])
+@pytest.mark.parametrize("remap", [False, True])
+def test_host_trace_equals_oracle(M, N, K, tile, order, G, mode, P, remap):
+    s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
+    got = ts.schedule_trace_host(M, N, K, s)
+    bm, bn, bk = (int(v) for v in tile.split("x"))
+    ref = osch.trace(M, N, K, bm, bn, bk, _oracle_sched(s, P))
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_host_trace_auto_grid_uses_cus_times_occupancy():
+    s = ts.Schedule(order="grouped", group_m=8, mode="persistent", tile="256x256x64")
+    got = ts.schedule_trace_host(8192, 8192, 4096, s, cu_count=256, programs_per_cu=1)
+    ref = osch.trace(8192, 8192, 4096, 256, 256, 64, _oracle_sched(s, 256))
+    assert np.array_equal(got, ref)
+    with pytest.raises(ts.TsError):
+        ts.schedule_trace_host(8192, 8192, 4096, s)  # no device and no CU count given

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (from the acceptance bound of oracle.gemm): |C_gpu - C*| <= 2.5e-4 * S + 1e-6,
+plus one unit in the last place of |C*| for 16-bit outputs.  Integer-valued
+inputs make every fp32 accumulation exact, so there the GPU result must equal
+the oracle's exact value rounded to the output type, bit for bit.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import gemm as og
+from tests.gpu_helpers import TORCH_OUT, round_to, sample_rows_cols, say, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import tile_scheduling_amd as ts
+else:  # collected on CPU-only hosts, never run there
+    ts = None
+
+TILES = ["64x64x32", "128x128x64", "256x256x64"]
+IO = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+
+
+def schedules(tile, P=256):
+    out = []
+    for (order, G), mode, remap in itertools.product([("row_major", 8), ("grouped", 8), ("grouped", 3)],
+                                                      ["tiled", "persistent", "crosstile"], [False, True]):
+        out.append(ts.Schedule(order=order, group_m=G, mode=mode, num_programs=0 if mode == "tiled" else P,
+                               xcd_remap=remap, tile=tile))
+    return out
+
+
+def run(A, B, ab, c_dtype, sched, M, N, K):
+    a, b = to_device(A, ab), to_device(B, ab)
+    say(f"gemm {M}x{N}x{K} {ab}->{c_dtype} {sched.label()}")
+    c = torch.full((M, N), float("nan"), dtype=TORCH_OUT[c_dtype], device="cuda")
+    ts.gemm(a, b, out=c, schedule=sched)
+    torch.cuda.synchronize()
+    return c
+
+
+def assert_accept(c_gpu, C, S, c_dtype, what=""):
+    ok, worst, bad = og.accept(c_gpu, C, S, c_dtype)
+    assert ok, f"{what}: {bad} outputs outside the bound (worst ratio {worst:.3g})"
+    return worst
+
+
+# ---- exactness with integer inputs ---------------------------------------------------
+
+SHAPES = {"64x64x32": (200, 300, 130), "128x128x64": (300, 390, 200), "256x256x64": (600, 700, 260)}
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("ab,c_dtype", IO)
+def test_integer_inputs_bit_exact(tile, ab, c_dtype):
+    M, N, K = SHAPES[tile]
+    A, B = workloads.pair(M, N, K, ab, "int", 500)
+    C, _ = og.gemm(A, B, ab, threads=4)
+    expect = round_to(C, c_dtype)
+    for sched in (ts.Schedule(tile=tile), ts.Schedule(order="grouped", group_m=3, mode="crosstile",
+                                                      num_programs=5, tile=tile)):
+        got = to_f64(run(A, B, ab, c_dtype, sched, M, N, K))
+        bad = np.argwhere(got != expect)
+        assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_aligned_integer_inputs_bit_exact(tile):
+    # whole tiles: the unmasked kernels
+    bm, bn, bk = (int(v) for v in tile.split("x"))
+    M, N, K = 2 * bm, 3 * bn, 4 * bk
+    A, B = workloads.pair(M, N, K, "f16", "int", 501)
+    C, _ = og.gemm(A, B, "f16")
+    assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == 0
+    for mode in ("tiled", "persistent", "crosstile"):
+        got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode=mode, num_programs=4, tile=tile), M, N, K))
+        assert np.array_equal(got, C), mode
+
+
+# ---- the 256^3 workload: 64x64x32 tiles, row-major, fp16 in, fp32 out ----------------
+
+def test_square_256_f16_f32_full_oracle():
+    w = workloads.SQUARE_256
+    A, B = workloads.inputs(w)
+    C, S = og.gemm(A, B, w.ab_dtype)
+    sched = ts.Schedule(order="row_major", mode="tiled", tile="64x64x32")
+    assert ts.query(w.M, w.N, w.K, sched, ts.TS_F16, ts.TS_F32)["grid"] == 16
+    got = to_f64(run(A, B, w.ab_dtype, w.c_dtype, sched, w.M, w.N, w.K))
+    worst = assert_accept(got, C, S, "f32", "256^3")
+    say(f"256^3 worst |err|/bound = {worst:.3g}")
+
+
+# ---- ragged shapes, every schedule, bit-identical across schedules -----------------
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("ab,c_dtype", IO)
+def test_ragged_every_schedule(tile, ab, c_dtype):
+    bm, bn, bk = (int(v) for v in tile.split("x"))
+    M, N, K = 3 * bm + 17, 4 * bn + 9, 5 * bk + 11   # several tiles and a ragged tail in M, N, K
+    A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 600)
+    C, S = og.gemm(A, B, ab, threads=4)
+    first = None
+    for sched in schedules(tile, P=5):
+        c = run(A, B, ab, c_dtype, sched, M, N, K)
+        if first is None:
+            first = c
+            assert_accept(to_f64(c), C, S, c_dtype, sched.label())
+        else:
+            assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
+
+
+# ---- the ragged bf16 workload at full size: all four schedules -----------------------
+
+def test_ragged_bf16_5000x12290x1000_full_size():
+    w = workloads.RAGGED_BF16
+    A, B = workloads.inputs(w)
+    rng = np.random.default_rng(7)
+    base = None
+    for sched in [ts.Schedule(tile="256x256x64"),
+                  ts.Schedule(order="grouped", group_m=8, tile="256x256x64"),
+                  ts.Schedule(order="grouped", group_m=8, mode="persistent", tile="256x256x64"),
+                  ts.Schedule(order="grouped", group_m=8, mode="crosstile", xcd_remap=True, tile="256x256x64"),
+                  ts.Schedule(order="grouped", group_m=16, mode="persistent", xcd_remap=True, tile="256x256x64")]:
+        q = ts.query(w.M, w.N, w.K, sched, ts.TS_BF16, ts.TS_F32)
+        assert q["masked"] == 1 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
+        c = run(A, B, w.ab_dtype, w.c_dtype, sched, w.M, w.N, w.K)
+        if base is None:
+            base = c
+        else:
+            assert torch.equal(c, base), sched.label()
+    rows, cols = sample_rows_cols(w.M, w.N, 256, 256, rng)
+    for r in rows:
+        C, S = og.gemm(A, B, w.ab_dtype, rows=(int(r), int(r) + 1))
+        assert_accept(to_f64(base[r:r + 1]), C, S, w.c_dtype, f"row {r}")
+    for cidx in cols:
+        C, S = og.gemm(A, B, w.ab_dtype, cols=(int(cidx), int(cidx) + 1), threads=8)
+        assert_accept(to_f64(base[:, cidx:cidx + 1]), C, S, w.c_dtype, f"col {cidx}")
+
+
+# ---- the large square workloads, in the launch configurations the benchmark times ----
+
+def _large(w, scheds):
+    A, B = workloads.inputs(w)
+    a, b = to_device(A, w.ab_dtype), to_device(B, w.ab_dtype)
+    base = None
+    for s in scheds:
+        say(f"gemm {w.name} {s.label()}")
+        c = torch.empty((w.M, w.N), dtype=TORCH_OUT[w.c_dtype], device="cuda")
+        ts.gemm(a, b, out=c, schedule=s)
+        torch.cuda.synchronize()
+        if base is None:
+            base = c
+        else:
+            assert torch.equal(c, base), s.label()
+            del c
+    rng = np.random.default_rng(11)
+    rows, cols = sample_rows_cols(w.M, w.N, 256, 256, rng, extra=3)
+    for r in rows[:10]:
+        C, S = og.gemm(A, B, w.ab_dtype, rows=(int(r), int(r) + 1))
+        assert_accept(to_f64(base[r:r + 1]), C, S, w.c_dtype, f"row {r}")
+    for cidx in cols[:6]:
+        C, S = og.gemm(A, B, w.ab_dtype, cols=(int(cidx), int(cidx) + 1), threads=8)
+        assert_accept(to_f64(base[:, cidx:cidx + 1]), C, S, w.c_dtype, f"col {cidx}")
+
+
+def test_8192x8192x4096_sampled():
+    _large(workloads.SQ_8192, [ts.Schedule(order=o, group_m=8, mode=m, xcd_remap=r)
+                               for o in ("row_major", "grouped") for m in ("tiled", "persistent")
+                               for r in (False, True)])
+
+
+def test_16384x16384x4096_sampled():
+    _large(workloads.SQ_16384, [ts.Schedule(order=o, group_m=g, mode=m, xcd_remap=r)
+                                for (o, g) in (("row_major", 8), ("grouped", 4), ("grouped", 8), ("grouped", 16))
+                                for m in ("tiled", "persistent", "crosstile") for r in (False, True)])
+
+
+@pytest.mark.parametrize("w", workloads.K_SWEEP[:4], ids=lambda w: w.name)
+def test_k_sweep_sampled(w):
+    _large(w, [ts.Schedule(order="grouped", group_m=8, mode="persistent", xcd_remap=True),
+               ts.Schedule(order="grouped", group_m=8, mode="crosstile", xcd_remap=True)])
+
+
+# ---- edge cases ---------------------------------------------------------------------------
+
+def test_empty_outputs_are_untouched():
+    c = torch.full((4, 4), 7.0, device="cuda")
+    a = torch.zeros((4, 8), dtype=torch.float16, device="cuda")
+    b = torch.zeros((8, 4), dtype=torch.float16, device="cuda")
+    assert ts.gemm_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), 0, 4, 8, c_dtype=ts.TS_F32) == ts.TS_OK
+    assert ts.gemm_raw(a.data_ptr(), b.data_ptr(), c.data_ptr(), 4, 0, 8, c_dtype=ts.TS_F32) == ts.TS_OK
+    torch.cuda.synchronize()
+    assert (c == 7.0).all()
+
+
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+@pytest.mark.parametrize("tile", TILES)
+def test_k_zero_writes_zeros(mode, tile):
+    a = torch.zeros((300, 0), dtype=torch.float16, device="cuda")
+    b = torch.zeros((0, 270), dtype=torch.float16, device="cuda")
+    c = torch.full((300, 270), float("nan"), dtype=torch.float16, device="cuda")
+    say(f"K=0 {mode} {tile}")
+    ts.gemm(a, b, out=c, schedule=ts.Schedule(mode=mode, num_programs=3, tile=tile))
+    torch.cuda.synchronize()
+    assert (c == 0).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (1, 777, 65), (513, 1, 33), (7, 9, 1), (65, 63, 8)])
+def test_tiny_shapes(M, N, K):
+    A, B = workloads.pair(M, N, K, "f16", "int", 70)
+    C, _ = og.gemm(A, B, "f16")
+    for tile in TILES:
+        got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode="crosstile", num_programs=2, tile=tile), M, N, K))
+        assert np.array_equal(got, C), tile
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_padded_and_unaligned_operands_with_canaries(tile):
+    M, N, K = 333, 290, 150
+    A, B = workloads.pair(M, N, K, "bf16", "int", 71)
+    C, _ = og.gemm(A, B, "bf16")
+    for pad, off in ((8, 0), (3, 1)):   # padded rows (aligned), then odd strides and odd offsets
+        abuf = torch.zeros((M, K + pad + off), dtype=torch.bfloat16, device="cuda")
+        bbuf = torch.zeros((K, N + pad + off), dtype=torch.bfloat16, device="cuda")
+        a = abuf[:, off:off + K]
+        b = bbuf[:, off:off + N]
+        a.copy_(to_device(A, "bf16"))
+        b.copy_(to_device(B, "bf16"))
+        cbuf = torch.full((M + 4, N + 2 * pad + 2 * off + 2), -12345.0, device="cuda")
+        c = cbuf[2:2 + M, pad + off:pad + off + N]
+        say(f"strided {tile} pad={pad} off={off}")
+        ts.gemm(a, b, out=c, schedule=ts.Schedule(order="grouped", group_m=2, mode="persistent",
+                                                  num_programs=3, tile=tile))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(c), C)
+        guard = cbuf.clone()
+        guard[2:2 + M, pad + off:pad + off + N] = -12345.0
+        assert (guard == -12345.0).all(), "write outside C"
+
+
+def test_deterministic():
+    A, B = workloads.pair(1000, 1100, 700, "f16", "uniform", 72)
+    s = ts.Schedule(order="grouped", group_m=4, mode="crosstile", xcd_remap=True)
+    c1 = run(A, B, "f16", "f16", s, 1000, 1100, 700)
+    c2 = run(A, B, "f16", "f16", s, 1000, 1100, 700)
+    assert torch.equal(c1, c2)

@@ -1,0 +1,51 @@
+"""GPU schedule trace: the device computes each workgroup's (tile, K step)
+sequence with the functions the GEMM kernels use; it must equal the oracle's
+integer maps bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import schedule as osch
+from tests.gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import tile_scheduling_amd as ts
+else:
+    ts = None
+
+
+def _oracle(M, N, K, s, grid):
+    q = ts.query(M, N, K, s)
+    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE}[s.mode]
+    order = osch.GROUPED if s.order == "grouped" else osch.ROW_MAJOR
+    os_ = osch.Schedule(order=order, group_m=s.group_m, mode=mode, num_programs=grid,
+                        xcd_remap=s.xcd_remap, xcds=q["xcds"])
+    return osch.trace(M, N, K, q["block_m"], q["block_n"], q["block_k"], os_)
+
+
+CASES = [(256, 256, 256, "64x64x32"), (5000, 12290, 1000, "256x256x64"), (8192, 8192, 4096, "256x256x64"),
+         (16384, 16384, 128, "256x256x64"), (1000, 700, 0, "128x128x64"), (300, 520, 200, "64x64x32")]
+
+
+@pytest.mark.parametrize("M,N,K,tile", CASES)
+@pytest.mark.parametrize("order,G", [("row_major", 8), ("grouped", 4), ("grouped", 8), ("grouped", 16)])
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+@pytest.mark.parametrize("remap", [False, True])
+def test_gpu_trace_equals_oracle(M, N, K, tile, order, G, mode, remap):
+    s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=0, xcd_remap=remap, tile=tile)
+    say(f"trace {M}x{N}x{K} {s.label()}")
+    got = ts.schedule_trace(M, N, K, s).numpy()
+    grid = ts.query(M, N, K, s)["grid"]
+    ref = _oracle(M, N, K, s, grid)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_device_properties_and_auto_grid():
+    q = ts.query(16384, 16384, 4096, ts.Schedule(mode="persistent"))
+    say(f"query {q}")
+    assert q["cu_count"] > 0 and q["programs_per_cu"] >= 1
+    assert q["grid"] == min(q["cu_count"] * q["programs_per_cu"], q["num_tiles"])
+    assert q["scratch_bytes"] >= 0 and q["vgprs"] > 0

@@ -1,0 +1,192 @@
+"""Python binding of libtsgemm (tiled GEMM with tile-order schedules, MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libtsgemm.so``.  PyTorch supplies device memory and streams.  The
+library is built in-tree by ``python -m tile_scheduling_amd.build``; importing
+this package without it raises ImportError, and there is no fallback path.
+
+    import torch, tile_scheduling_amd as ts
+    c = ts.gemm(a, b, out_dtype=torch.float16,
+                schedule=ts.Schedule(order="grouped", group_m=8, mode="persistent"))
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch  # loaded first: libtsgemm binds to the HIP runtime torch already loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtsgemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tile_scheduling_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+# status codes, element types and schedule enums (include/tsgemm.h)
+TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_ALIGNMENT, TS_ERR_HIP, TS_ERR_NO_DEVICE = 0, -1, -2, -3, -4, -5
+TS_F16, TS_BF16, TS_F32 = 1, 2, 3
+ORDERS = {"row_major": 0, "grouped": 1}
+MODES = {"tiled": 0, "persistent": 1, "crosstile": 2}
+TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3}
+
+
+class _Schedule(ctypes.Structure):
+    _fields_ = [("order", _i32), ("group_m", _i32), ("mode", _i32),
+                ("num_programs", _i32), ("xcd_remap", _i32), ("tile_config", _i32)]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [("block_m", _i32), ("block_n", _i32), ("block_k", _i32), ("threads", _i32),
+                ("num_m_tiles", _i64), ("num_n_tiles", _i64), ("k_steps", _i64), ("num_tiles", _i64),
+                ("grid", _i64), ("programs_per_cu", _i32), ("cu_count", _i32), ("xcds", _i32),
+                ("lds_bytes", _i32), ("masked", _i32), ("vgprs", _i32), ("scratch_bytes", _i32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib.ts_gemm.argtypes = [_p, _p, _p] + [_i64] * 9 + [_i32, _i32, ctypes.POINTER(_Schedule), _p]
+_lib.ts_gemm.restype = _i32
+_lib.ts_schedule_trace.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule), _p, _i64, _p]
+_lib.ts_schedule_trace.restype = _i32
+_lib.ts_schedule_trace_host.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule),
+                                        _i32, _i32, _p, _i64]
+_lib.ts_schedule_trace_host.restype = _i32
+_lib.ts_query.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule), ctypes.POINTER(LaunchInfo)]
+_lib.ts_query.restype = _i32
+_lib.ts_status_string.argtypes = [_i32]
+_lib.ts_status_string.restype = ctypes.c_char_p
+
+EXPORTS = ("ts_gemm", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query", "ts_status_string")
+
+
+class TsError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(status_string(status))
+
+
+def status_string(status: int) -> str:
+    return _lib.ts_status_string(int(status)).decode()
+
+
+@dataclasses.dataclass(frozen=True)
+class Schedule:
+    """Tile order and mode of one launch (see ts_schedule in include/tsgemm.h)."""
+
+    order: str = "row_major"      # "row_major" | "grouped"
+    group_m: int = 8              # GROUP_SIZE_M for the grouped order
+    mode: str = "tiled"           # "tiled" | "persistent" | "crosstile"
+    num_programs: int = 0         # persistent grid; 0 = CUs x workgroups per CU
+    xcd_remap: bool = False       # contiguous tile-id runs per XCD
+    tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64"
+
+    def _c(self) -> _Schedule:
+        return _Schedule(ORDERS[self.order], int(self.group_m), MODES[self.mode],
+                         int(self.num_programs), 1 if self.xcd_remap else 0, TILES[self.tile])
+
+    def label(self) -> str:
+        o = "rowmajor" if self.order == "row_major" else f"grouped{self.group_m}"
+        r = "+remap" if self.xcd_remap else ""
+        p = f"/P{self.num_programs}" if self.mode != "tiled" and self.num_programs else ""
+        return f"{o}{r}/{self.mode}{p}/{self.tile}"
+
+
+_TORCH_DTYPE = {torch.float16: TS_F16, torch.bfloat16: TS_BF16, torch.float32: TS_F32}
+
+
+def _check(status: int):
+    if status != TS_OK:
+        raise TsError(status)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gemm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+         out_dtype: torch.dtype | None = None, schedule: Schedule | None = None) -> torch.Tensor:
+    """C = A @ B with A [M,K], B [K,N] fp16/bf16 CUDA tensors; C fp16/bf16/fp32.
+
+    Enqueued on the current stream of A's device; returns C (``out`` if given).
+    """
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shapes {tuple(a.shape)} @ {tuple(b.shape)} do not multiply")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("A and B must be on the same GPU")
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or a.dtype, device=a.device)
+    elif out.shape != (M, N) or out.device != a.device:
+        raise ValueError("out has the wrong shape or device")
+    s = (schedule or Schedule())._c()
+    st = _lib.ts_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                      a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
+                      _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0), ctypes.byref(s),
+                      _stream_handle(a.device))
+    _check(st)
+    return out
+
+
+def gemm_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int,
+             strides=(None, 1, None, 1, None, 1), ab_dtype: int = TS_F16, c_dtype: int = TS_F16,
+             schedule: Schedule | None = None, stream: int = 0) -> int:
+    """Direct call of ts_gemm with integer pointers; returns the status code."""
+    sam, sak, sbk, sbn, scm, scn = strides
+    sam = K if sam is None else sam
+    sbk = N if sbk is None else sbk
+    scm = N if scm is None else scm
+    s = (schedule or Schedule())._c()
+    return _lib.ts_gemm(a_ptr, b_ptr, c_ptr, M, N, K, sam, sak, sbk, sbn, scm, scn,
+                        ab_dtype, c_dtype, ctypes.byref(s), stream)
+
+
+def query(M: int, N: int, K: int, schedule: Schedule | None = None,
+          ab_dtype: int = TS_F16, c_dtype: int = TS_F16) -> dict:
+    info = LaunchInfo()
+    s = (schedule or Schedule())._c()
+    _check(_lib.ts_query(M, N, K, ab_dtype, c_dtype, ctypes.byref(s), ctypes.byref(info)))
+    return info.as_dict()
+
+
+def schedule_trace(M: int, N: int, K: int, schedule: Schedule | None = None,
+                   ab_dtype: int = TS_F16, c_dtype: int = TS_F16, device: int | str = "cuda"):
+    """GPU-computed work sequence of every workgroup, as an int32 [rows, 5] CPU tensor."""
+    info = query(M, N, K, schedule, ab_dtype, c_dtype)
+    ksp = max(info["k_steps"], 1)
+    grid = info["grid"]
+    rows = grid * (-(-info["num_tiles"] // grid) * ksp if grid else 0)
+    out = torch.empty((max(rows, 1), 5), dtype=torch.int32, device=device)
+    s = (schedule or Schedule())._c()
+    _check(_lib.ts_schedule_trace(M, N, K, ab_dtype, c_dtype, ctypes.byref(s), out.data_ptr(), rows,
+                                  _stream_handle(out.device)))
+    torch.cuda.synchronize(out.device)
+    return out[:rows].cpu()
+
+
+def schedule_trace_host(M: int, N: int, K: int, schedule: Schedule, cu_count: int = 0,
+                        programs_per_cu: int = 0, ab_dtype: int = TS_F16, c_dtype: int = TS_F16):
+    """The same work sequence computed by the library on the CPU (no GPU needed).
+
+    In persistent modes with num_programs == 0, cu_count * programs_per_cu stands
+    in for the device's grid.
+    """
+    import numpy as np
+
+    sized = schedule
+    if schedule.mode != "tiled" and schedule.num_programs == 0:
+        sized = dataclasses.replace(schedule, num_programs=cu_count * programs_per_cu)
+    info = query(M, N, K, sized, ab_dtype, c_dtype)
+    grid, T = info["grid"], info["num_tiles"]
+    rows = grid * (-(-T // grid) * max(info["k_steps"], 1)) if grid else 0
+    out = np.full((max(rows, 1), 5), -7, dtype=np.int32)
+    s = schedule._c()
+    _check(_lib.ts_schedule_trace_host(M, N, K, ab_dtype, c_dtype, ctypes.byref(s), cu_count,
+                                       programs_per_cu, out.ctypes.data, rows))
+    return out[:rows]

@@ -1,0 +1,328 @@
+// C-ABI of the tiled GEMM library: argument validation, launch planning (tile
+// configuration, grid, masking), dispatch to the kernel instances, and the
+// schedule trace.  See include/tsgemm.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "../../include/tsgemm.h"
+#include "internal.hpp"
+
+namespace ts {
+
+__global__ void trace_kernel(SchedArgs s, int mode, int max_items, int32_t* out) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < s.grid) trace_program(s, mode, p, max_items, out + (long long)p * max_items * 5);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int cu_count = 0;
+    int xcds = 8;
+};
+
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+
+// Properties of the current device, queried once per device.
+ts_status current_device(int* dev_out, DeviceInfo* info) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return TS_ERR_NO_DEVICE;
+    }
+    std::call_once(g_dev_once[dev], [dev]() {
+        int cus = 0, x = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x < 1 || x > 64) x = 8;
+        (void)hipGetLastError();
+        g_dev[dev].cu_count = cus;
+        g_dev[dev].xcds = x;
+    });
+    if (g_dev[dev].cu_count <= 0) return TS_ERR_NO_DEVICE;
+    *dev_out = dev;
+    *info = g_dev[dev];
+    return TS_OK;
+}
+
+struct Plan {
+    int cfg;                // CFG_*
+    int bm, bn, bk;
+    int io;                 // IO_*
+    int mode;
+    bool masked;
+    int vec_a, vec_b, vec_c;
+    SchedArgs s;            // grid filled once the device is known (persistent auto)
+    int requested_programs; // 0 = auto
+    int64_t max_items;
+};
+
+void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
+    switch (cfg) {
+        case CFG_64: *bm = Cfg64::BM; *bn = Cfg64::BN; *bk = Cfg64::BK; break;
+        case CFG_128: *bm = Cfg128::BM; *bn = Cfg128::BN; *bk = Cfg128::BK; break;
+        default: *bm = Cfg256::BM; *bn = Cfg256::BN; *bk = Cfg256::BK; break;
+    }
+}
+
+KernelRef kernel_of(const Plan& p) {
+    switch (p.cfg) {
+        case CFG_64: return kernels_cfg64(p.io, p.masked, p.mode);
+        case CFG_128: return kernels_cfg128(p.io, p.masked, p.mode);
+        default: return kernels_cfg256(p.io, p.masked, p.mode);
+    }
+}
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape-only checks and choices, shared by every entry point.  Row strides and
+// base addresses (which only ts_gemm has) refine the vector flags later.
+ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, const ts_schedule* sp,
+                     Plan* p) {
+    if (M < 0 || N < 0 || K < 0) return TS_ERR_INVALID_ARG;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return TS_ERR_UNSUPPORTED;
+    if (ab == TS_F16 && c == TS_F16) p->io = IO_F16_F16;
+    else if (ab == TS_F16 && c == TS_F32) p->io = IO_F16_F32;
+    else if (ab == TS_BF16 && c == TS_BF16) p->io = IO_BF16_BF16;
+    else if (ab == TS_BF16 && c == TS_F32) p->io = IO_BF16_F32;
+    else if ((ab == TS_F16 || ab == TS_BF16 || ab == TS_F32) && (c == TS_F16 || c == TS_BF16 || c == TS_F32))
+        return TS_ERR_UNSUPPORTED;
+    else
+        return TS_ERR_INVALID_ARG;
+
+    ts_schedule s = {TS_ORDER_ROW_MAJOR, 1, TS_MODE_TILED, 0, 0, TS_TILE_AUTO};
+    if (sp) s = *sp;
+    if (s.order != TS_ORDER_ROW_MAJOR && s.order != TS_ORDER_GROUPED) return TS_ERR_INVALID_ARG;
+    if (s.order == TS_ORDER_GROUPED && s.group_m < 1) return TS_ERR_INVALID_ARG;
+    if (s.mode != TS_MODE_TILED && s.mode != TS_MODE_PERSISTENT && s.mode != TS_MODE_CROSSTILE)
+        return TS_ERR_INVALID_ARG;
+    if (s.num_programs < 0) return TS_ERR_INVALID_ARG;
+    if (s.xcd_remap != 0 && s.xcd_remap != 1) return TS_ERR_INVALID_ARG;
+    if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64) return TS_ERR_INVALID_ARG;
+
+    int cfg = s.tile_config;
+    if (cfg == TS_TILE_AUTO) {
+        // largest tile that still gives the chip at least half a wave of tiles
+        if (cdiv64(M, 256) * cdiv64(N, 256) >= 128) cfg = CFG_256;
+        else if (cdiv64(M, 128) * cdiv64(N, 128) >= 128) cfg = CFG_128;
+        else cfg = CFG_64;
+    }
+    p->cfg = cfg;
+    cfg_dims(cfg, &p->bm, &p->bn, &p->bk);
+    const int64_t nm = cdiv64(M, p->bm), nn = cdiv64(N, p->bn), ks = cdiv64(K, p->bk);
+    if (nm * nn > INT_MAX / 2 || ks > INT_MAX / 2) return TS_ERR_UNSUPPORTED;
+    p->mode = s.mode;
+    p->requested_programs = s.num_programs;
+    p->s.nm = (int)nm;
+    p->s.nn = (int)nn;
+    p->s.ks = (int)ks;
+    p->s.num_tiles = (int)(nm * nn);
+    p->s.order = s.order;
+    p->s.group_m = s.order == TS_ORDER_GROUPED ? (int)(s.group_m < nm ? s.group_m : (nm > 0 ? nm : 1)) : 1;
+    p->s.remap = s.xcd_remap;
+    p->s.xcds = 8;
+    p->s.grid = 0;
+    // dense, 16-byte aligned operands assumed until ts_gemm sees the real ones
+    const int64_t c_elem = c == TS_F32 ? 4 : 2;
+    p->vec_a = (K % 8) == 0;
+    p->vec_b = (N % 8) == 0;
+    p->vec_c = (N * c_elem) % 16 == 0;
+    p->masked = (M % p->bm) != 0 || (N % p->bn) != 0 || (K % p->bk) != 0 || K == 0 ||
+                !p->vec_a || !p->vec_b || !p->vec_c;
+    return TS_OK;
+}
+
+// Workgroups one CU holds for the plan's kernel (needs a device).
+int programs_per_cu(const Plan& p) {
+    const KernelRef k = kernel_of(p);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k.fn, k.threads, 0) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    return n;
+}
+
+// Resolve the grid; cu/ppc of 0 mean "unknown" (host-only callers must pass
+// num_programs explicitly in persistent modes).
+ts_status resolve_grid(Plan* p, int cu_count, int ppc, int xcds) {
+    p->s.xcds = xcds > 0 ? xcds : 8;
+    if (p->s.num_tiles == 0) {
+        p->s.grid = 0;
+        p->max_items = 0;
+        return TS_OK;
+    }
+    if (p->mode == TS_MODE_TILED) {
+        p->s.grid = p->s.num_tiles;
+    } else {
+        int64_t P = p->requested_programs;
+        if (P == 0) {
+            if (cu_count <= 0 || ppc <= 0) return TS_ERR_NO_DEVICE;
+            P = (int64_t)cu_count * ppc;
+        }
+        p->s.grid = (int)(P < p->s.num_tiles ? P : p->s.num_tiles);
+    }
+    const int64_t ksp = p->s.ks > 0 ? p->s.ks : 1;
+    p->max_items = cdiv64(p->s.num_tiles, p->s.grid) * ksp;
+    return TS_OK;
+}
+
+}  // namespace
+}  // namespace ts
+
+using namespace ts;
+
+extern "C" const char* ts_status_string(ts_status status) {
+    switch (status) {
+        case TS_OK: return "TS_OK";
+        case TS_ERR_INVALID_ARG: return "TS_ERR_INVALID_ARG: invalid argument";
+        case TS_ERR_UNSUPPORTED: return "TS_ERR_UNSUPPORTED: unsupported dtype pair, stride pattern or size";
+        case TS_ERR_ALIGNMENT: return "TS_ERR_ALIGNMENT: pointer not aligned to its element size";
+        case TS_ERR_HIP: return "TS_ERR_HIP: HIP runtime error";
+        case TS_ERR_NO_DEVICE: return "TS_ERR_NO_DEVICE: no usable GPU";
+    }
+    return "unknown ts_status";
+}
+
+extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                             int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                             int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
+                             const ts_schedule* sched, void* stream) {
+    Plan p;
+    ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
+    if (st != TS_OK) return st;
+    if (M == 0 || N == 0) return TS_OK;
+    if (!C || (K > 0 && (!A || !B))) return TS_ERR_INVALID_ARG;
+    if (stride_ak != 1 || stride_bn != 1 || stride_cn != 1) return TS_ERR_UNSUPPORTED;
+    if ((M > 1 && K > 0 && stride_am < K) || (K > 1 && stride_bk < N) || (M > 1 && stride_cm < N))
+        return TS_ERR_INVALID_ARG;
+    if (stride_am < 0 || stride_bk < 0 || stride_cm < 0) return TS_ERR_INVALID_ARG;
+    if (stride_am > INT_MAX || stride_bk > INT_MAX || stride_cm > INT_MAX) return TS_ERR_UNSUPPORTED;
+    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
+    const int c_elem = c_dtype == TS_F32 ? 4 : 2;
+    if ((a & 1) || (b & 1) || (c % c_elem)) return TS_ERR_ALIGNMENT;
+
+    // 16-byte operand vectors need 16-byte aligned rows; C vectors are 4 elements.
+    p.vec_a = (a % 16 == 0) && (stride_am % 8 == 0 || M == 1);
+    p.vec_b = (b % 16 == 0) && (stride_bk % 8 == 0 || K <= 1);
+    p.vec_c = (c % (4 * c_elem) == 0) && (stride_cm % 4 == 0 || M == 1);
+    p.masked = (M % p.bm) != 0 || (N % p.bn) != 0 || (K % p.bk) != 0 || K == 0 || !p.vec_a || !p.vec_b ||
+               !p.vec_c;
+
+    int dev;
+    DeviceInfo di;
+    st = current_device(&dev, &di);
+    if (st != TS_OK) return st;
+    const int ppc = (p.mode != TS_MODE_TILED && p.requested_programs == 0) ? programs_per_cu(p) : 1;
+    st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
+    if (st != TS_OK) return st;
+
+    GemmArgs g;
+    g.A = static_cast<const uint16_t*>(A);
+    g.B = static_cast<const uint16_t*>(B);
+    g.C = C;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.lda = stride_am;
+    g.ldb = stride_bk;
+    g.ldc = stride_cm;
+    g.vec_a = p.vec_a;
+    g.vec_b = p.vec_b;
+    g.vec_c = p.vec_c;
+    g.s = p.s;
+    const KernelRef k = kernel_of(p);
+    void* args[] = {&g};
+    if (hipLaunchKernel(k.fn, dim3(p.s.grid), dim3(k.threads), args, 0, (hipStream_t)stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return TS_ERR_HIP;
+    }
+    return TS_OK;
+}
+
+extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                              const ts_schedule* sched, ts_launch_info* out) {
+    if (!out) return TS_ERR_INVALID_ARG;
+    Plan p;
+    ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
+    if (st != TS_OK) return st;
+    int dev;
+    DeviceInfo di;
+    const bool have_dev = current_device(&dev, &di) == TS_OK;
+    const int ppc = have_dev ? programs_per_cu(p) : 0;
+    st = resolve_grid(&p, have_dev ? di.cu_count : 0, ppc, have_dev ? di.xcds : 8);
+    if (st != TS_OK) return st;
+    const KernelRef k = kernel_of(p);
+    out->block_m = p.bm;
+    out->block_n = p.bn;
+    out->block_k = p.bk;
+    out->threads = k.threads;
+    out->num_m_tiles = p.s.nm;
+    out->num_n_tiles = p.s.nn;
+    out->k_steps = p.s.ks;
+    out->num_tiles = p.s.num_tiles;
+    out->grid = p.s.grid;
+    out->programs_per_cu = ppc;
+    out->cu_count = have_dev ? di.cu_count : 0;
+    out->xcds = p.s.xcds;
+    out->lds_bytes = k.lds_bytes;
+    out->masked = p.masked ? 1 : 0;
+    out->vgprs = -1;
+    out->scratch_bytes = -1;
+    if (have_dev) {
+        hipFuncAttributes fa;
+        if (hipFuncGetAttributes(&fa, k.fn) == hipSuccess) {
+            out->vgprs = fa.numRegs;
+            out->scratch_bytes = (int32_t)fa.localSizeBytes;
+            out->lds_bytes = (int32_t)fa.sharedSizeBytes;
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    return TS_OK;
+}
+
+extern "C" ts_status ts_schedule_trace_host(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                                            const ts_schedule* sched, int32_t cu_count, int32_t ppc,
+                                            int32_t* out, int64_t out_rows) {
+    Plan p;
+    ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
+    if (st != TS_OK) return st;
+    st = resolve_grid(&p, cu_count, ppc, 8);
+    if (st != TS_OK) return st;
+    const int64_t need = (int64_t)p.s.grid * p.max_items;
+    if (need == 0) return TS_OK;
+    if (!out || out_rows < need) return TS_ERR_INVALID_ARG;
+    for (int prog = 0; prog < p.s.grid; ++prog)
+        trace_program(p.s, p.mode, prog, (int)p.max_items, out + (int64_t)prog * p.max_items * 5);
+    return TS_OK;
+}
+
+extern "C" ts_status ts_schedule_trace(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                                       const ts_schedule* sched, int32_t* out, int64_t out_rows, void* stream) {
+    Plan p;
+    ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
+    if (st != TS_OK) return st;
+    int dev;
+    DeviceInfo di;
+    st = current_device(&dev, &di);
+    if (st != TS_OK) return st;
+    const int ppc = (p.mode != TS_MODE_TILED && p.requested_programs == 0) ? programs_per_cu(p) : 1;
+    st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
+    if (st != TS_OK) return st;
+    const int64_t need = (int64_t)p.s.grid * p.max_items;
+    if (need == 0) return TS_OK;
+    if (!out || out_rows < need) return TS_ERR_INVALID_ARG;
+    if (need * 5 > INT_MAX) return TS_ERR_UNSUPPORTED;
+    const int threads = 256;
+    hipLaunchKernelGGL(trace_kernel, dim3((p.s.grid + threads - 1) / threads), dim3(threads), 0,
+                       (hipStream_t)stream, p.s, p.mode, (int)p.max_items, out);
+    if (hipGetLastError() != hipSuccess) return TS_ERR_HIP;
+    return TS_OK;
+}

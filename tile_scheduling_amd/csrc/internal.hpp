@@ -1,0 +1,52 @@
+// Declarations shared by the kernel-instance files and the C-ABI implementation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_kernel.hpp"
+
+namespace ts {
+
+// Input/output type pair of a kernel instance.
+enum : int { IO_F16_F16 = 0, IO_F16_F32 = 1, IO_BF16_BF16 = 2, IO_BF16_F32 = 3 };
+
+// Tile configurations (same numbering as TS_TILE_* in tsgemm.h).
+enum : int { CFG_64 = 1, CFG_128 = 2, CFG_256 = 3 };
+
+typedef TileCfg<64, 64, 32, 2, 2> Cfg64;
+typedef TileCfg<128, 128, 64, 2, 2> Cfg128;
+typedef TileCfg<256, 256, 64, 2, 2> Cfg256;
+
+struct KernelRef {
+    const void* fn;  // __global__ function, launched with one GemmArgs argument
+    int threads;
+    int lds_bytes;   // static LDS of the instance
+};
+
+template <class Cfg, class TI, class TO, bool MK>
+const void* kernel_by_mode(int mode) {
+    switch (mode) {
+        case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, MK, MODE_TILED>);
+        case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, MK, MODE_PERSISTENT>);
+        default: return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, MK>);
+    }
+}
+
+template <class Cfg>
+KernelRef kernel_for(int io, bool masked, int mode) {
+    const void* f = nullptr;
+    switch (io) {
+        case IO_F16_F16: f = masked ? kernel_by_mode<Cfg, InF16, OutF16, true>(mode) : kernel_by_mode<Cfg, InF16, OutF16, false>(mode); break;
+        case IO_F16_F32: f = masked ? kernel_by_mode<Cfg, InF16, OutF32, true>(mode) : kernel_by_mode<Cfg, InF16, OutF32, false>(mode); break;
+        case IO_BF16_BF16: f = masked ? kernel_by_mode<Cfg, InBF16, OutBF16, true>(mode) : kernel_by_mode<Cfg, InBF16, OutBF16, false>(mode); break;
+        default: f = masked ? kernel_by_mode<Cfg, InBF16, OutF32, true>(mode) : kernel_by_mode<Cfg, InBF16, OutF32, false>(mode); break;
+    }
+    return KernelRef{f, Cfg::NT, Cfg::LDS_BYTES};
+}
+
+// One function per tile configuration, each defined in its own translation unit.
+KernelRef kernels_cfg64(int io, bool masked, int mode);
+KernelRef kernels_cfg128(int io, bool masked, int mode);
+KernelRef kernels_cfg256(int io, bool masked, int mode);
+
+}  // namespace ts

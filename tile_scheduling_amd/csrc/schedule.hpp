@@ -1,0 +1,143 @@
+// Tile-order schedules shared by the GEMM kernels, the trace kernel and the
+// host-side trace.  Every function here is __host__ __device__ so that the
+// schedule a kernel follows and the schedule the library reports are the same
+// code.
+//
+// Orders
+//   row-major ("(1/n) Triton matmul ... persistent kernel", naive tiled listing):
+//     tile_m = t / num_n_tiles, tile_n = t % num_n_tiles.
+//   grouped ("(2/n) ... grouped ordering (CTA swizzle)", section Implementation):
+//     tiles are dealt in groups of G tile rows; group g covers rows
+//     [g*G, g*G + gs) with gs = min(G, num_m_tiles - g*G) (the last group may be
+//     short) and, inside a group, consecutive ids walk down the gs rows of one
+//     tile column before moving to the next column.
+// Modes
+//   tiled: workgroup w computes tile id w.
+//   persistent ("(1/n) ...", naive persistent listing): P workgroups; workgroup p
+//     computes ids p, p+P, ... below num_tiles.
+//   flattened cross-tile ("(3/n) ... cross tile pipelining"): the same ids and K
+//     steps as persistent, walked as one loop whose counter k wraps to 0 after
+//     the last K step of a tile.
+// XCD remap (this library's addition; not on the pages): MI355X deals the
+//   workgroups of a launch round-robin over its 8 XCDs, each with a private L2.
+//   Renumbering w -> (w % X) * q + min(w % X, r) + w / X (q = n / X, r = n % X)
+//   gives XCD x one contiguous run of logical ids, so that neighbouring tiles in
+//   the chosen order share an L2.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TS_HD __host__ __device__ __forceinline__
+#else
+#define TS_HD inline
+#endif
+
+namespace ts {
+
+enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
+enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2 };
+
+// Everything a program needs to find its tiles.  Plain integers, passed by value
+// to kernels.  `group_m` is already clamped to [1, nm] by the host (values above
+// nm give the same map as nm and would only risk overflow in group_m * nn).
+struct SchedArgs {
+    int nm, nn;        // tile grid: cdiv(M, BM), cdiv(N, BN)
+    int ks;            // K steps: cdiv(K, BK)
+    int num_tiles;     // nm * nn
+    int order;         // ORDER_*
+    int group_m;       // G in [1, nm]
+    int grid;          // programs launched (P, or num_tiles when tiled)
+    int remap;         // XCD remap on/off
+    int xcds;          // XCDs the dispatcher deals workgroups over
+};
+
+TS_HD int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+TS_HD int min_i(int a, int b) { return a < b ? a : b; }
+
+TS_HD int xcd_remap(int w, int n, int X) {
+    const int q = n / X, r = n % X, x = w % X;
+    return x * q + min_i(x, r) + w / X;
+}
+
+TS_HD void tile_coords(const SchedArgs& s, int t, int& tm, int& tn) {
+    if (s.order == ORDER_GROUPED) {
+        const int in_group = s.group_m * s.nn;            // tiles per full group
+        const int gid = t / in_group;
+        const int tig = t - gid * in_group;               // id inside the group
+        const int first_m = gid * s.group_m;
+        const int gs = min_i(s.group_m, s.nm - first_m);  // rows in this group
+        tm = first_m + tig % gs;
+        tn = tig / gs;
+    } else {
+        tm = t / s.nn;
+        tn = t - tm * s.nn;
+    }
+}
+
+// The work of one program: tile ids start, start + grid, ... below num_tiles,
+// each with max(ks, 1) K steps.  ks == 0 (K == 0) keeps one step per tile so
+// that the tile is still written (with zeros).
+struct ProgramWork {
+    int start;   // first logical tile id
+    int step;    // distance between consecutive tile ids of this program
+    int ntiles;  // tiles this program computes
+    int ksp;     // K steps per tile, at least 1
+
+    TS_HD ProgramWork(const SchedArgs& s, int program) {
+        start = s.remap ? xcd_remap(program, s.grid, s.xcds) : program;
+        step = s.grid;
+        ntiles = start < s.num_tiles ? cdiv_i(s.num_tiles - start, s.grid) : 0;
+        ksp = s.ks > 0 ? s.ks : 1;
+    }
+    TS_HD int tile_id(int i) const { return start + i * step; }
+    TS_HD int total_items() const { return ntiles * ksp; }
+};
+
+// Cursor of the flattened loop: (tile id, k) advanced one K step at a time;
+// after the last K step of a tile, k wraps to 0 and the tile id moves on by P.
+struct FlatCursor {
+    int tile;
+    int k;
+    TS_HD FlatCursor(const ProgramWork& w) : tile(w.start), k(0) {}
+    TS_HD bool last_k(const ProgramWork& w) const { return k == w.ksp - 1; }
+    TS_HD void advance(const ProgramWork& w) {
+        if (k == w.ksp - 1) {
+            k = 0;
+            tile += w.step;
+        } else {
+            ++k;
+        }
+    }
+};
+
+// One program's trace rows (p, it, tile_m, tile_n, k) into rows[0 .. max_items),
+// padded with -1.  The nested walk is used for tiled and persistent modes, the
+// flattened cursor for the cross-tile mode, exactly as the kernels do.
+TS_HD void trace_program(const SchedArgs& s, int mode, int program, int max_items, int32_t* rows) {
+    const ProgramWork w(s, program);
+    int it = 0;
+    if (mode == MODE_CROSSTILE) {
+        FlatCursor c(w);
+        for (int n = w.total_items(); it < n; ++it) {
+            int tm, tn;
+            tile_coords(s, c.tile, tm, tn);
+            int32_t* r = rows + 5 * it;
+            r[0] = program; r[1] = it; r[2] = tm; r[3] = tn; r[4] = c.k;
+            c.advance(w);
+        }
+    } else {
+        for (int i = 0; i < w.ntiles; ++i) {
+            int tm, tn;
+            tile_coords(s, w.tile_id(i), tm, tn);
+            for (int k = 0; k < w.ksp; ++k, ++it) {
+                int32_t* r = rows + 5 * it;
+                r[0] = program; r[1] = it; r[2] = tm; r[3] = tn; r[4] = k;
+            }
+        }
+    }
+    for (; it < max_items; ++it)
+        for (int f = 0; f < 5; ++f) rows[5 * it + f] = -1;
+}
+
+}  // namespace ts

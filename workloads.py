@@ -75,7 +75,7 @@ SQUARE_256 = Workload("gemm_256x256x256_f16_f32", 256, 256, 256, "f16", "f32", "
 SQ_8192 = Workload("gemm_8192x8192x4096_f16", 8192, 8192, 4096, "f16", "f16", "uniform", 1001)
 SQ_16384 = Workload("gemm_16384x16384x4096_f16", 16384, 16384, 4096, "f16", "f16", "uniform", 1002)
 K_SWEEP = tuple(
-    Workload(f"gemm_16384x16384x{k}_f16", 16384, 16384, k, "f16", "f16", "uniform", 1003)
+    Workload(f"gemm_16384x16384x{k}_f16_ksweep", 16384, 16384, k, "f16", "f16", "uniform", 1003)
     for k in (128, 512, 1024, 2048, 4096)
 )
 RAGGED_BF16 = Workload("gemm_5000x12290x1000_bf16_f32", 5000, 12290, 1000, "bf16", "f32", "normal", 1004)
