@@ -128,6 +128,46 @@ def cpu_baseline(A, B, w, budget_s: float):
                       f"in {t:.1f} s on {threads} threads"}
 
 
+PMC_SCHEDULES = {
+    "gemm_16384x16384x4096_f16": [f"{o}{r}/{m}" for o in ("rowmajor", "grouped4", "grouped8", "grouped16")
+                                  for r in ("", "+remap") for m in ("tiled", "persistent")],
+    "gemm_8192x8192x4096_f16": [f"{o}{r}/{m}" for o in ("rowmajor", "grouped8")
+                                for r in ("", "+remap") for m in ("tiled", "persistent")],
+}
+
+
+def pmc_target(ts, torch, np, workloads):
+    """Launch sequence for counter passes: a fill and a copy of 1 GiB each (known
+    HBM bytes, to scale the counters), then two launches of every schedule in
+    PMC_SCHEDULES.  Prints a manifest line per dispatch in launch order."""
+    n = 1 << 29  # 2-byte elements: 1 GiB per buffer
+    x = torch.empty(n, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    torch.cuda.synchronize()
+    print("dispatch fill 1073741824 write", flush=True)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print("dispatch copy 1073741824 read+write", flush=True)
+    del x, y
+    by_name = {w.name: w for w in workloads.ALL}
+    for name, labels in PMC_SCHEDULES.items():
+        w = by_name[name]
+        A, B = workloads.inputs(w)
+        in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
+        a = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
+        b = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
+        c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        torch.cuda.synchronize()
+        for lab in labels:
+            s = parse_schedule(lab)
+            for rep in range(2):
+                ts.gemm(a, b, out=c, schedule=s)
+                torch.cuda.synchronize()
+                print(f"dispatch gemm {name} {s.label()} rep{rep}", flush=True)
+        del a, b, c
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +178,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-target", action="store_true",
+                    help="run the fixed launch sequence used for hardware-counter passes and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -152,6 +194,9 @@ def main():
     import workloads
 
     by_name = {w.name: w for w in workloads.ALL}
+    if args.pmc_target:
+        pmc_target(ts, torch, np, workloads)
+        return
     w = by_name[args.workload]
     out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.c_dtype]
     in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
