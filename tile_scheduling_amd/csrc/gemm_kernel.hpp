@@ -7,30 +7,41 @@
 // masked store) and the merged loop of "(3/n) ... cross tile pipelining".  How
 // it is computed is this file's own design for MI355X:
 //
-//  * A workgroup owns a BM x BN output tile and walks K in BK slices.  Each slice
-//    of A (BM x BK) and B (BK x BN) is staged in LDS in a two-slot ring: while
-//    the MFMAs consume slot s, the next slice is already in flight from global
-//    memory into registers and lands in slot s^1 before the single barrier of
-//    the step.
+//  * A workgroup owns a BM x BN output tile and walks K in BK slices.  Slices of
+//    A (BM x BK) and B (BK x BN) are staged in LDS in a two-slot ring: while the
+//    MFMAs consume slot s, the next slice travels from global memory into
+//    registers and is written into slot s^1 before the single barrier of the
+//    step.
 //  * Both operands sit in LDS "K-contiguous": A as [m][k] (its natural layout),
 //    B transposed to [n][k] on the way in (each loader thread reads an 8x8 or 4x8
 //    (k x n) block with 16-byte row loads and transposes it in registers with
 //    byte permutes), so that every MFMA operand fragment is one 16-byte LDS read.
-//    16-byte chunks of each LDS row are XOR-swizzled by the row index so that the
-//    8 lanes served together by the LDS touch 8 different bank groups on both
-//    the writes and the fragment reads.
+//    The 16-byte chunks of each LDS row are XOR-swizzled by the row index (A:
+//    row mod 8; B: (row mod 8) ^ (row/8 mod 4)) so that the 8 lanes served
+//    together by the LDS touch 8 different bank groups on the fragment reads,
+//    the A writes and (up to a factor of two) the B writes.  The swizzle term of
+//    a fragment read depends only on the lane, so each lane keeps one LDS offset
+//    per K sub-step and every read is that offset plus an immediate.
 //  * The product uses v_mfma_f32_32x32x16_{f16,bf16}.  The operands are fed as
 //    (B fragment, A fragment), so each 32x32 accumulator block holds C^T: a lane
 //    owns 4 consecutive columns of one row, and the epilogue writes 8- or
 //    16-byte vectors.
 //  * Waves are arranged WM x WN over the tile; wave (wm, wn) owns a (BM/WM) x
-//    (BN/WN) sub-tile of FM x FN accumulator blocks.
+//    (BN/WN) sub-tile of FM x FN accumulator blocks.  Fragments of K sub-step
+//    s+1 are read from LDS while the MFMAs of sub-step s run; the last few MFMAs
+//    of a K step are issued after the barrier, behind the first LDS reads of the
+//    next slot.
+//  * Global loads use a wave-uniform base pointer per row group plus one 32-bit
+//    per-lane offset (the address arithmetic is scalar).
 //  * Tile order and the persistent / flattened loops come from schedule.hpp; the
 //    trace kernel runs the same functions.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "schedule.hpp"
 
@@ -65,22 +76,25 @@ struct TileCfg {
     static constexpr int NT = 64 * WM * WN;             // threads
     static constexpr int TM = BM / WM, TN = BN / WN;    // wave sub-tile
     static constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 blocks per wave
+    static constexpr int SUB = BK / 16;                 // MFMA K sub-steps per slice
     static constexpr int KCH = BK / 8;                  // 16-byte chunks per LDS row
     static constexpr int NA = BM * KCH;                 // A chunks per slice
     static constexpr int CA = (NA + NT - 1) / NT;       // A chunks per thread
     static constexpr int KBH = (BK * BN / 64 >= NT) ? 8 : 4;  // k rows of a B loader block
     static constexpr int NB = (BK / KBH) * (BN / 8);    // B loader blocks per slice
     static constexpr int CB = (NB + NT - 1) / NT;       // B blocks per thread
-    static constexpr int SLOT = (BM + BN) * BK;         // halfwords per ring slot
-    static constexpr int LDS_BYTES = 2 * SLOT * 2;
+    static constexpr int ROW_BYTES = BK * 2;            // one LDS row (m or n) of a slice
+    static constexpr int A_SLOT = BM * ROW_BYTES, B_SLOT = BN * ROW_BYTES;
+    static constexpr int B_BASE = 2 * A_SLOT;           // LDS: [A0][A1][B0][B1]
+    static constexpr int LDS_BYTES = 2 * (A_SLOT + B_SLOT);
+    static constexpr int HOLD = (FM * FN >= 8) ? 8 : FM * FN / 2;  // MFMAs issued after the barrier
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tile must be whole 32x32 blocks");
-    static_assert(BK % 16 == 0 && (KCH & (KCH - 1)) == 0, "BK must be 16 * power of two");
-    static_assert(BK % KBH == 0, "BK must be a multiple of the B block height");
+    static_assert(BK % 16 == 0 && KCH <= 8 && (KCH & (KCH - 1)) == 0, "BK must be 16, 32 or 64");
+    static_assert(BK % KBH == 0 && NT % KCH == 0, "loader shape");
+    static_assert(A_SLOT <= 65535 && SUB % 2 == 0 || SUB == 1, "slot offsets must fit LDS immediates");
 };
 
 // ---- small device helpers ------------------------------------------------------
-
-__device__ __forceinline__ int swz(int row, int kch) { return (row ^ (row >> 3)) & (kch - 1); }
 
 template <class TI>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
@@ -96,8 +110,10 @@ __device__ __forceinline__ f32x16 mfma32<InBF16>(u32x4 a, u32x4 b, f32x16 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t pack_bits(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
 // Output element conversion (round to nearest even) and stores of 4 consecutive
-// columns; `full` = all 4 inside N with an aligned address.
+// columns; `vec` = all 4 inside N at an aligned address.
 template <class TO> struct Out;
 template <> struct Out<OutF32> {
     typedef float T;
@@ -115,8 +131,8 @@ template <> struct Out<OutF16> {
         _Float16 h[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
         if (vec && valid >= 4) {
             u32x2 w;
-            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+            w[0] = pack_bits(__builtin_bit_cast(uint16_t, h[0]), __builtin_bit_cast(uint16_t, h[1]));
+            w[1] = pack_bits(__builtin_bit_cast(uint16_t, h[2]), __builtin_bit_cast(uint16_t, h[3]));
             *reinterpret_cast<u32x2*>(p) = w;
         } else {
             for (int e = 0; e < 4; ++e) if (e < valid) p[e] = h[e];
@@ -129,8 +145,8 @@ template <> struct Out<OutBF16> {
         __bf16 h[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         if (vec && valid >= 4) {
             u32x2 w;
-            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
+            w[0] = pack_bits(__builtin_bit_cast(uint16_t, h[0]), __builtin_bit_cast(uint16_t, h[1]));
+            w[1] = pack_bits(__builtin_bit_cast(uint16_t, h[2]), __builtin_bit_cast(uint16_t, h[3]));
             *reinterpret_cast<u32x2*>(p) = w;
         } else {
             for (int e = 0; e < 4; ++e) if (e < valid) p[e] = h[e];
@@ -152,28 +168,131 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int valid, bool
     return r;
 }
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ u32x4 lds_read16(const char* lds, uint32_t off) {
+    return *reinterpret_cast<const u32x4*>(lds + off);
+}
+
 // ---- the tile engine -------------------------------------------------------------
 
+// Pipelines (per K step of 64 MFMAs per wave on LDS slot SLOT):
+//  fast (unmasked, BK = 64): A arrives by direct-to-LDS buffer loads issued at
+//    sub-step 0 into slot SLOT^1 (one slice ahead); B travels two slices ahead in
+//    registers and is transposed into slot SLOT^1 at sub-step 1.  Before the
+//    step's barrier each wave waits for its own loads.
+//  register (masked edges, or BK = 32): A and B one slice ahead in registers,
+//    written into slot SLOT^1 at the last sub-steps.
 template <class Cfg, class TI, class TO, bool MASKED>
 struct Engine {
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
-    static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH;
+    static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH, SUB = Cfg::SUB;
     static constexpr int CA = Cfg::CA, CB = Cfg::CB, KBH = Cfg::KBH;
+    static constexpr int RB = Cfg::ROW_BYTES;
+    static constexpr int NW = NT / 64;               // waves
+    static constexpr int NMF = FM * FN;              // MFMAs per sub-step
+    static constexpr int A_ROWS_PER_C = NT / KCH;    // A rows between a thread's chunks
+    static constexpr int NBN = BN / 8;               // B loader blocks along n
+    static constexpr bool A_DMA = !MASKED && RB == 128 && (BM * RB) % (1024 * NW) == 0;
+    static constexpr int A_DMA_N = A_DMA ? BM * RB / 1024 / NW : 0;  // 1 KiB DMA loads per wave
+    static constexpr int B_DIST = A_DMA ? 2 : 1;     // B slices in flight in registers
+    static constexpr int A_SETS = A_DMA ? 0 : 1;
+    // sub-steps that write the next slice into LDS
+    static constexpr int A_STORE_S = SUB > 2 ? SUB - 2 : SUB - 1;       // register path only
+    static constexpr int B_STORE_S = A_DMA ? (SUB > 1 ? 1 : 0) : SUB - 1;
+    static_assert(CB == 1, "one B loader block per thread");
 
     const GemmArgs& g;
-    uint16_t* lds;     // ring of two slots: [A: BM x BK][B: BN x BK] each
-    int tid, lane, wm, wn;
+    char* lds;
+    int tid, lane, wm, wn, wave;
 
-    u32x4 ra[CA];          // A slice in flight
-    u32x4 rb[CB][KBH];     // B slice in flight (KBH rows of 8 columns per block)
+    // per-lane LDS byte offsets
+    uint32_t a_rd[SUB];   // fragment read of block 0 at sub-step s (block i: + i*32*RB)
+    uint32_t b_rd[SUB];
+    uint32_t a_wr[2];     // A chunk c (register path): a_wr[c&1] + c*A_ROWS_PER_C*RB
+    uint32_t b_wr[8];     // B write j of the loader block
+    uint32_t b_sel[2];    // byte-permute selector of B writes with even / odd j
+    // per-lane global byte offsets
+    uint32_t a_go[2], b_go;   // A: [c&1] of the load / chunk index c
+    bool b_active;        // this thread owns a B loader block
+
+    u32x4 ra[A_SETS > 0 ? A_SETS : 1][CA];   // A slice in flight (register path)
+    u32x4 rb[B_DIST][KBH];                   // B slices in flight (KBH rows of 8 columns)
+    u32x4 fa[2][FM], fb[2][FN];
     f32x16 acc[FM][FN];
 
-    __device__ __forceinline__ Engine(const GemmArgs& g_, uint16_t* lds_) : g(g_), lds(lds_) {
+    __device__ __forceinline__ Engine(const GemmArgs& g_, char* lds_) : g(g_), lds(lds_) {
         tid = threadIdx.x;
         lane = tid & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         wm = wave / Cfg::WN;
         wn = wave % Cfg::WN;
+        const int r32 = lane & 31, hk = lane >> 5;
+        // Rows of both operands are swizzled by swz(r) = (r ^ (r >> 3)) mod KCH.  A
+        // fragment row is (32-aligned base) + r32, so swz depends on r32 and, for
+        // KCH = 8, on bit 0 of the block index (bit 5 of the row), which flips chunk
+        // bit 2, i.e. sub-step s <-> s ^ 2: odd blocks use the offset of s ^ 2.
+        const int sw = (r32 ^ (r32 >> 3)) & (KCH - 1);
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            const int ch = 2 * s + hk;
+            a_rd[s] = (uint32_t)((wm * Cfg::TM + r32) * RB + ((ch ^ sw) * 16));
+            b_rd[s] = (uint32_t)(Cfg::B_BASE + (wn * Cfg::TN + r32) * RB + ((ch ^ sw) * 16));
+        }
+        if (A_DMA) {
+            // lane l of a 1 KiB load lands at row (8 * grp + l/8), chunk l%8 of the
+            // slot and fetches the logical chunk the swizzle puts there; grp mod 8
+            // = 4 * (c mod 2) + wave, so even and odd loads c differ in chunk bit 2
+            const int row = lane >> 3, pc = lane & 7;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int grp7 = (4 * e + wave) & 7;
+                a_go[e] = (uint32_t)(((long long)row * g.lda + ((pc ^ row ^ grp7) * 8)) * 2);
+                a_wr[e] = 0;
+            }
+        } else {
+            // A chunk (row, kc) of this thread; chunk c adds c * A_ROWS_PER_C rows,
+            // which changes the swizzle only through bit 2 for odd c (KCH = 8)
+            const int row = tid / KCH, kc = tid % KCH;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = row + e * A_ROWS_PER_C;
+                a_wr[e] = (uint32_t)(r * RB + ((kc ^ ((r ^ (r >> 3)) & (KCH - 1))) * 16)) - e * A_ROWS_PER_C * RB;
+                a_go[e] = (uint32_t)(((long long)row * g.lda + kc * 8) * 2);
+            }
+        }
+        {   // B loader block (kb, nb) of this thread.  Write instruction j of lane
+            // group half h = (nb >> 3) & 1 stores column j ^ h, so that the 16 lanes
+            // served together cover both row parities and 16 distinct bank groups.
+            const int nb = tid % NBN, kb = tid / NBN;
+            const int h = (nb >> 3) & 1;
+            b_active = Cfg::NB % NT == 0 || tid < Cfg::NB;
+            b_sel[0] = h ? 0x07060302u : 0x05040100u;   // even j: half (j ^ h) & 1
+            b_sel[1] = h ? 0x05040100u : 0x07060302u;   // odd j
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = nb * 8 + (j ^ h);
+                const int swz = (n ^ (n >> 3)) & (KCH - 1);
+                if (KBH == 8)
+                    b_wr[j] = (uint32_t)(Cfg::B_BASE + n * RB + ((kb ^ swz) * 16));
+                else
+                    b_wr[j] = (uint32_t)(Cfg::B_BASE + n * RB + ((((kb >> 1) ^ swz)) * 16) + (kb & 1) * 8);
+            }
+            b_go = (uint32_t)(((long long)kb * KBH * g.ldb + nb * 8) * 2);
+        }
+        // Keep the lane offsets opaque: otherwise their compile-time parts (the B
+        // region starts at 64 KiB) are folded into per-access constants too large
+        // for the 16-bit LDS offset field, and every access needs its own register.
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            asm volatile("" : "+v"(a_rd[s]));
+            asm volatile("" : "+v"(b_rd[s]));
+        }
+        asm volatile("" : "+v"(a_wr[0]));
+        asm volatile("" : "+v"(a_wr[1]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(b_wr[j]));
     }
 
     __device__ __forceinline__ void zero_acc() {
@@ -185,104 +304,308 @@ struct Engine {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
-    // Global -> registers: slice k of tile (m0, n0).
-    __device__ __forceinline__ void load_slice(int m0, int n0, int k) {
+    // Scalar-register buffer resource over `p`; zero records when `valid` is false,
+    // which turns every load through it into a zero with no memory access.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* p, bool valid) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
+                                                 __builtin_amdgcn_readfirstlane(valid ? -1 : 0), kBufferFlags);
+    }
+
+    // A slice k of tile row m0 straight into LDS slot SLOT (fast path).
+    template <int SLOT>
+    __device__ __forceinline__ void dma_a(int m0, int k, bool valid) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
+#pragma unroll
+        for (int c = 0; c < A_DMA_N; ++c) {
+            const int grp = c * NW + wave;                     // 8-row group (1 KiB)
+            const int soff = (int)((long long)grp * 8 * g.lda * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(lds + SLOT * Cfg::A_SLOT + grp * 1024), 16,
+                (int)a_go[c & 1], soff, 0, 0);
+        }
+    }
+
+    // A slice k of tile row m0 into registers (register path).
+    __device__ __forceinline__ void load_a(int m0, int k, bool valid) {
         const int k0 = k * BK;
+        if (!MASKED) {
+            const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k0, valid);
+#pragma unroll
+            for (int c = 0; c < CA; ++c) {
+                const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
+                ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)a_go[0], soff, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             const int idx = c * NT + tid;
             const int row = idx / KCH, kc = idx % KCH;
             const int gm = m0 + row, gk = k0 + kc * 8;
             const uint16_t* p = g.A + (long long)gm * g.lda + gk;
-            if (!MASKED) {
-                ra[c] = *reinterpret_cast<const u32x4*>(p);
-            } else {
-                const bool in = (Cfg::NA % NT == 0 || idx < Cfg::NA) && gm < g.M;
-                ra[c] = in ? load8_masked(p, g.K - gk, g.vec_a) : u32x4{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int idx = c * NT + tid;
-            const int nb = idx % (BN / 8), kb = idx / (BN / 8);
-            const int gn = n0 + nb * 8, gk = k0 + kb * KBH;
-            const bool blk = Cfg::NB % NT == 0 || idx < Cfg::NB;
-#pragma unroll
-            for (int r = 0; r < KBH; ++r) {
-                const uint16_t* p = g.B + (long long)(gk + r) * g.ldb + gn;
-                if (!MASKED) {
-                    rb[c][r] = blk ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
-                } else {
-                    rb[c][r] = (blk && gk + r < g.K) ? load8_masked(p, g.N - gn, g.vec_b)
-                                                     : u32x4{0, 0, 0, 0};
-                }
-            }
+            const bool in = valid && (Cfg::NA % NT == 0 || idx < Cfg::NA) && gm < g.M;
+            ra[0][c] = in ? load8_masked(p, g.K - gk, g.vec_a) : u32x4{0, 0, 0, 0};
         }
     }
 
-    // Registers -> LDS slot; B is transposed to [n][k] on the way.
-    __device__ __forceinline__ void store_slice(int slot) {
-        uint16_t* sa = lds + slot * Cfg::SLOT;
-        uint16_t* sb = sa + BM * BK;
+    // B slice k of tile column n0 into register set SET.
+    template <int SET>
+    __device__ __forceinline__ void load_b(int n0, int k, bool valid) {
+        const int k0 = k * BK;
+        if (!MASKED) {
+            const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k0 * g.ldb + n0, valid);
+#pragma unroll
+            for (int q = 0; q < KBH; ++q) {
+                const int soff = (int)(q * g.ldb * 2);
+                // threads without a B block re-read thread 0's block (in bounds);
+                // the value is never stored
+                rb[SET][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
+            }
+            return;
+        }
+        const int nb = tid % NBN, kb = tid / NBN;
+        const int gn = n0 + nb * 8, gk = k0 + kb * KBH;
+#pragma unroll
+        for (int q = 0; q < KBH; ++q) {
+            const uint16_t* p = g.B + (long long)(gk + q) * g.ldb + gn;
+            rb[SET][q] = (valid && b_active && gk + q < g.K) ? load8_masked(p, g.N - gn, g.vec_b)
+                                                            : u32x4{0, 0, 0, 0};
+        }
+    }
+
+    // Register A slice -> LDS slot SLOT (register path).
+    template <int SLOT>
+    __device__ __forceinline__ void store_a() {
+        char* sa = lds + SLOT * Cfg::A_SLOT;
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
-            const int idx = c * NT + tid;
-            if (Cfg::NA % NT == 0 || idx < Cfg::NA) {
-                const int row = idx / KCH, kc = idx % KCH;
-                *reinterpret_cast<u32x4*>(sa + row * BK + ((kc ^ swz(row, KCH)) * 8)) = ra[c];
-            }
+            if (Cfg::NA % NT == 0 || c * NT + tid < Cfg::NA)
+                *reinterpret_cast<u32x4*>(sa + a_wr[c & 1] + c * A_ROWS_PER_C * RB) = ra[0][c];
         }
+    }
+
+    // Register set SET -> LDS slot SLOT (B part), transposed to [n][k].
+    template <int SET, int SLOT>
+    __device__ __forceinline__ void store_b() {
+        if (!(Cfg::NB % NT == 0) && !b_active) return;
+        char* sb = lds + SLOT * Cfg::B_SLOT;
 #pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            const int idx = c * NT + tid;
-            if (!(Cfg::NB % NT == 0 || idx < Cfg::NB)) continue;
-            const int nb = idx % (BN / 8), kb = idx / (BN / 8);
+        for (int j = 0; j < 8; ++j) {
+            // column j ^ h of the block: element j ^ h of every loaded row (both sit
+            // in dword j >> 1; the lane's selector picks the half)
+            const int d = j >> 1;
+            const uint32_t sel = b_sel[j & 1];
+            if (KBH == 8) {
+                u32x4 col;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // column j of the block: element j of every loaded row
-                const int d = j >> 1;
-                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                const int n = nb * 8 + j;
-                if (KBH == 8) {
-                    u32x4 col;
+                for (int q = 0; q < 4; ++q)
+                    col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
+                *reinterpret_cast<u32x4*>(sb + b_wr[j]) = col;
+            } else {
+                u32x2 col;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        col[q] = __builtin_amdgcn_perm(rb[c][2 * q + 1][d], rb[c][2 * q][d], sel);
-                    *reinterpret_cast<u32x4*>(sb + n * BK + ((kb ^ swz(n, KCH)) * 8)) = col;
-                } else {
-                    u32x2 col;
-#pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        col[q] = __builtin_amdgcn_perm(rb[c][2 * q + 1][d], rb[c][2 * q][d], sel);
-                    *reinterpret_cast<u32x2*>(sb + n * BK + (((kb >> 1) ^ swz(n, KCH)) * 8) + (kb & 1) * 4) = col;
-                }
+                for (int q = 0; q < 2; ++q)
+                    col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
+                *reinterpret_cast<u32x2*>(sb + b_wr[j]) = col;
             }
         }
     }
 
-    // MFMAs over one LDS slot.
-    __device__ __forceinline__ void compute(int slot) {
-        const uint16_t* sa = lds + slot * Cfg::SLOT;
-        const uint16_t* sb = sa + BM * BK;
-        const int r32 = lane & 31, hk = lane >> 5;
+    template <int SLOT>
+    __device__ __forceinline__ void read_frags(int s, int buf) {
+        const char* base_a = lds + SLOT * Cfg::A_SLOT;
+        const char* base_b = lds + SLOT * Cfg::B_SLOT;
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int ch = 2 * s + hk;
-            u32x4 af[FM], bf[FN];
+        for (int i = 0; i < FM; ++i) fa[buf][i] = lds_read16(base_a, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * Cfg::TM + i * 32 + r32;
-                af[i] = *reinterpret_cast<const u32x4*>(sa + row * BK + ((ch ^ swz(row, KCH)) * 8));
+        for (int j = 0; j < FN; ++j) fb[buf][j] = lds_read16(base_b, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
+    }
+
+    // Fragment number idx (A blocks first, then B blocks) of sub-step s.
+    template <int SLOT>
+    __device__ __forceinline__ void read_frag(int s, int idx, int buf) {
+        if (idx < FM) {
+            const int i = idx;
+            fa[buf][i] = lds_read16(lds + SLOT * Cfg::A_SLOT, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
+        } else {
+            const int j = idx - FM;
+            fb[buf][j] = lds_read16(lds + SLOT * Cfg::B_SLOT, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
+        }
+    }
+
+    // Write j of register set SET into B slot SLOT (column j ^ h, see b_wr).
+    template <int SET, int SLOT>
+    __device__ __forceinline__ void store_b_one(int j) {
+        if (!(Cfg::NB % NT == 0) && !b_active) return;
+        char* sb = lds + SLOT * Cfg::B_SLOT;
+        const int d = j >> 1;
+        const uint32_t sel = b_sel[j & 1];
+        if (KBH == 8) {
+            u32x4 col;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
+            *reinterpret_cast<u32x4*>(sb + b_wr[j]) = col;
+        } else {
+            u32x2 col;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
+            *reinterpret_cast<u32x2*>(sb + b_wr[j]) = col;
+        }
+    }
+
+    // MFMA number t of a sub-step, in (i, j) order.
+    __device__ __forceinline__ void mfma_one(int buf, int t) {
+        const int i = t / FN, j = t % FN;
+        acc[i][j] = mfma32<TI>(fb[buf][j], fa[buf][i], acc[i][j]);
+    }
+
+    // MFMAs number [first, last) of a sub-step, in (i, j) order.
+    __device__ __forceinline__ void mfmas(int buf, int first, int last) {
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+            if (t < first || t >= last) continue;
+            const int i = t / FN, j = t % FN;
+            acc[i][j] = mfma32<TI>(fb[buf][j], fa[buf][i], acc[i][j]);
+        }
+    }
+
+    // Where the next slices come from: `a` one slice ahead (tile row origin m0,
+    // slice ka), `b` B_DIST slices ahead (tile column origin n0, slice kb).  A
+    // false `*valid` means past the last slice: nothing is read and zeros flow.
+    struct Next {
+        int m0, ka;
+        bool va;
+        int n0, kb;
+        bool vb;
+    };
+
+    // Sub-step S of a K step on slot SLOT.  On the unmasked path every MFMA slot
+    // carries at most one fragment read for the next sub-step plus one global load
+    // (sub-step 0) or one LDS write (store sub-steps), in a fixed order enforced by
+    // scheduling barriers, so that no burst of memory instructions stalls the
+    // wave's issue while the matrix unit has nothing queued.
+    template <int SLOT, int S>
+    __device__ __forceinline__ void substep(const Next& nx) {
+        constexpr int b = S & 1;
+        constexpr bool last = S + 1 == SUB;
+        constexpr int nmf = last ? NMF - Cfg::HOLD : NMF;
+        constexpr int BSET = B_DIST == 2 ? SLOT : 0;         // set receiving B loads
+        constexpr int BSTORE = B_DIST == 2 ? (SLOT ^ 1) : 0;  // set written into slot SLOT^1
+        constexpr int NFR = last ? 0 : FM + FN;              // fragment reads to spread
+        if (MASKED) {
+            if (S == 0) {
+                load_b<BSET>(nx.n0, nx.kb, nx.vb);
+                load_a(nx.m0, nx.ka, nx.va);
             }
+            if (!last) read_frags<SLOT>(S + 1, b ^ 1);
+            if (S == A_STORE_S) store_a<SLOT ^ 1>();
+            if (S == B_STORE_S) store_b<BSTORE, SLOT ^ 1>();
+            mfmas(b, 0, nmf);
+            __builtin_amdgcn_sched_barrier(0);
+            return;
+        }
+        // unmasked: resources and scalar offsets first
+        __amdgpu_buffer_rsrc_t rb_rsrc, ra_rsrc;
+        if (S == 0) {
+            rb_rsrc = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            ra_rsrc = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+        }
+        constexpr int NVM = KBH + (A_DMA ? A_DMA_N : CA);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * Cfg::TN + j * 32 + r32;
-                bf[j] = *reinterpret_cast<const u32x4*>(sb + row * BK + ((ch ^ swz(row, KCH)) * 8));
+        for (int t = 0; t < (nmf > NFR ? nmf : NFR); ++t) {
+            if (t < nmf) mfma_one(b, t);
+            if (t < NFR) read_frag<SLOT>(S + 1 < SUB ? S + 1 : 0, t, b ^ 1);
+            if (S == 0 && t < NVM) {
+                if (t < KBH) {
+                    const int soff = (int)(t * g.ldb * 2);
+                    rb[BSET][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rb_rsrc, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
+                } else if (A_DMA) {
+                    const int c = t - KBH;
+                    const int grp = c * NW + wave;
+                    const int soff = (int)((long long)grp * 8 * g.lda * 2);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        ra_rsrc, (__attribute__((address_space(3))) void*)(lds + (SLOT ^ 1) * Cfg::A_SLOT + grp * 1024),
+                        16, (int)a_go[c & 1], soff, 0, 0);
+                } else {
+                    const int c = t - KBH;
+                    const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
+                    ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)a_go[0], soff, 0);
+                }
             }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<TI>(bf[j], af[i], acc[i][j]);
+            if (S == B_STORE_S && t < 8) store_b_one<BSTORE, SLOT ^ 1>(t);
+            if (!A_DMA && S == A_STORE_S && t < CA) {
+                if (Cfg::NA % NT == 0 || t * NT + tid < Cfg::NA)
+                    *reinterpret_cast<u32x4*>(lds + (SLOT ^ 1) * Cfg::A_SLOT + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[0][t];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    template <int SLOT, int... S>
+    __device__ __forceinline__ void substeps(const Next& nx, std::integer_sequence<int, S...>) {
+        (substep<SLOT, S>(nx), ...);
+    }
+
+    // One K step over LDS slot SLOT (fragments of its sub-step 0 already in buffer
+    // 0).  Slot SLOT^1, which every wave finished reading before the last barrier,
+    // receives the next slice; after this step's barrier its sub-step 0 fragments
+    // are read, behind the last HOLD MFMAs of this step.  Past the last slice these
+    // writes and reads carry zeros nobody uses, so every step has the same shape
+    // and the accumulators stay in one set of registers through the loop.
+    template <int SLOT>
+    __device__ __forceinline__ void kstep(const Next& nx) {
+        constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
+        substeps<SLOT>(nx, std::make_integer_sequence<int, SUB>{});
+        if (A_DMA) {
+            // each wave's direct-to-LDS loads must have landed before the barrier
+            // that hands the slot to the other waves (the B loads of this step,
+            // issued just before them, are waited for with them)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        read_frags<SLOT ^ 1>(0, 0);
+        mfmas(LB, NMF - Cfg::HOLD, NMF);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Prologue: slice 0 in slot 0 with its first fragments read; the fast path also
+    // starts B slice 1 (register set 1).  `nx` then describes the first step's loads.
+    __device__ __forceinline__ void prologue(int m0, int n0, int k0, int n1, int k1, bool two) {
+        load_b<0>(n0, k0, true);
+        if (A_DMA) {
+            dma_a<0>(m0, k0, true);
+            load_b<B_DIST - 1>(n1, k1, two);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+            load_a(m0, k0, true);
+            store_a<0>();
+        }
+        store_b<0, 0>();
+        __syncthreads();
+        read_frags<0>(0, 0);
+    }
+
+    // Full pipeline for one tile (no epilogue): steps alternate slots 0 and 1; an
+    // odd step count runs one slot-0 step first and then pairs starting on slot 1.
+    __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
+        prologue(m0, n0, 0, n0, 1, ks > 1);
+        auto nx = [&](int k) {  // loads issued by step k
+            return Next{m0, k + 1, k + 1 < ks, n0, k + B_DIST, k + B_DIST < ks};
+        };
+        int k = 0;
+        if (ks & 1) {
+            kstep<0>(nx(0));
+            for (k = 1; k < ks; k += 2) {
+                kstep<1>(nx(k));
+                kstep<0>(nx(k + 1));
+            }
+        } else {
+            for (; k < ks; k += 2) {
+                kstep<0>(nx(k));
+                kstep<1>(nx(k + 1));
+            }
         }
     }
 
@@ -310,6 +633,9 @@ struct Engine {
                         if (valid > 0) Out<TO>::store4(crow + n, v, valid, g.vec_c);
                     }
                 }
+                // one block at a time: keeps the accumulator reads from being hoisted
+                // into one burst that needs 256 more registers
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -318,10 +644,10 @@ struct Engine {
 // ---- kernels -------------------------------------------------------------------------
 
 // Tiled and persistent modes: for each of the program's tiles, a full pipeline
-// (prologue load, K loop with one slice in flight, epilogue).
+// (prologue loads, K loop with two slices in flight, epilogue).
 template <class Cfg, class TI, class TO, bool MASKED, int MODE>
 __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::SLOT];
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
     Engine<Cfg, TI, TO, MASKED> e(g, lds);
     const ProgramWork w(g.s, blockIdx.x);
     const int ntiles = (MODE == MODE_TILED) ? 1 : w.ntiles;
@@ -330,57 +656,75 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
         tile_coords(g.s, w.tile_id(i), tm, tn);
         const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
         e.zero_acc();
-        if (g.s.ks > 0) {
-            e.load_slice(m0, n0, 0);
-            e.store_slice(0);
-            __syncthreads();
-            for (int k = 0; k < g.s.ks; ++k) {
-                const int cur = k & 1;
-                const bool more = k + 1 < g.s.ks;
-                if (more) e.load_slice(m0, n0, k + 1);
-                e.compute(cur);
-                if (more) e.store_slice(cur ^ 1);
-                __syncthreads();
-            }
-        }
+        if (!MASKED || g.s.ks > 0) e.tile_mainloop(m0, n0, g.s.ks);
         e.store_tile(m0, n0);
     }
 }
 
-// Flattened cross-tile mode: one loop over (tile, k) items; the slice of item
-// it+1 -- the first slice of the next tile when item it ends a tile -- is in
-// flight while item it is multiplied and, at a tile's last K step, stored.
+// Position of the flattened loop: cursor plus the origin of its tile.
+struct FlatPos {
+    FlatCursor c;
+    int m0, n0;
+    template <class Cfg>
+    __device__ __forceinline__ void coords(const SchedArgs& s) {
+        int tm, tn;
+        tile_coords(s, c.tile, tm, tn);
+        m0 = tm * Cfg::BM;
+        n0 = tn * Cfg::BN;
+    }
+    template <class Cfg>
+    __device__ __forceinline__ void advance(const SchedArgs& s, const ProgramWork& w) {
+        const int t = c.tile;
+        c.advance(w);
+        if (c.tile != t) coords<Cfg>(s);
+    }
+};
+
+// Flattened cross-tile mode: one loop over (tile, k) items.  The slices of the
+// next items -- the first slices of the next tile when item it ends a tile -- are
+// in flight while item it is multiplied and, at a tile's last K step, stored.
 template <class Cfg, class TI, class TO, bool MASKED>
 __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::SLOT];
-    Engine<Cfg, TI, TO, MASKED> e(g, lds);
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    typedef Engine<Cfg, TI, TO, MASKED> E;
+    E e(g, lds);
     const ProgramWork w(g.s, blockIdx.x);
     const int total = w.total_items();
     if (total == 0) return;
-    FlatCursor cur(w);
-    int tm, tn;
-    tile_coords(g.s, cur.tile, tm, tn);
-    e.load_slice(tm * Cfg::BM, tn * Cfg::BN, cur.k);
-    e.store_slice(0);
-    __syncthreads();
-    for (int it = 0; it < total; ++it) {
-        const int slot = it & 1;
-        if (cur.k == 0) e.zero_acc();
-        FlatCursor nxt = cur;
-        nxt.advance(w);
-        int ntm = tm, ntn = tn;
-        const bool more = it + 1 < total;
-        if (more) {
-            if (nxt.tile != cur.tile) tile_coords(g.s, nxt.tile, ntm, ntn);
-            e.load_slice(ntm * Cfg::BM, ntn * Cfg::BN, nxt.k);
+    FlatPos cp{FlatCursor(w), 0, 0};   // item being multiplied
+    cp.template coords<Cfg>(g.s);
+    FlatPos la = cp;                   // next item whose A slice is loaded (one ahead)
+    la.template advance<Cfg>(g.s, w);
+    e.prologue(cp.m0, cp.n0, cp.c.k, la.n0, la.c.k, total > 1);
+    FlatPos lb = la;                   // next item whose B slice is loaded (B_DIST ahead)
+    if (E::B_DIST == 2) lb.template advance<Cfg>(g.s, w);
+    // cursors past the program's last item produce coordinates that are never read
+
+    int it = 0;
+    auto step = [&](auto slot_tag) {
+        constexpr int SLOT = decltype(slot_tag)::value;
+        if (cp.c.k == 0) e.zero_acc();
+        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + 1 < total, lb.n0, lb.c.k,
+                                                it + E::B_DIST < total});
+        la.template advance<Cfg>(g.s, w);
+        lb.template advance<Cfg>(g.s, w);
+        if (cp.c.last_k(w)) e.store_tile(cp.m0, cp.n0);
+        cp.template advance<Cfg>(g.s, w);
+        ++it;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (total & 1) {
+        step(S0{});
+        while (it < total) {
+            step(S1{});
+            step(S0{});
         }
-        e.compute(slot);
-        if (cur.last_k(w)) e.store_tile(tm * Cfg::BM, tn * Cfg::BN);
-        if (more) e.store_slice(slot ^ 1);
-        __syncthreads();
-        cur = nxt;
-        tm = ntm;
-        tn = ntn;
+    } else {
+        while (it < total) {
+            step(S0{});
+            step(S1{});
+        }
     }
 }
 
