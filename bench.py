@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 METRIC = "fp16 GEMM TFLOPS (2MNK/s) + % MFMA peak at M=N=16384, K=4096"
-DEFAULT_SCHEDULE = "grouped8+remap/tiled"
+DEFAULT_SCHEDULE = "grouped8+remap/persistent"
 KERNEL_SOURCES = ["tile_scheduling_amd/csrc/gemm_kernel.hpp", "tile_scheduling_amd/csrc/schedule.hpp",
                   "tile_scheduling_amd/csrc/internal.hpp"]
 
@@ -240,7 +240,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.ab_dtype, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.ab_dtype, "acc": "f32",
                    "out": w.c_dtype, "inputs": f"{w.dist} seed {w.seed}", "schedule": sched.label(),
-                   "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "grid": q["grid"]},
+                   "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "threads": q["threads"],
+                   "grid": q["grid"]},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

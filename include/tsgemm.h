@@ -76,7 +76,8 @@ enum {
     TS_TILE_AUTO = 0,          /* library chooses from the shape */
     TS_TILE_64x64x32 = 1,
     TS_TILE_128x128x64 = 2,
-    TS_TILE_256x256x64 = 3
+    TS_TILE_256x256x64 = 3,    /* 4 waves of 128x128 (one per SIMD)  */
+    TS_TILE_256x256x64_W8 = 4  /* 8 waves of 128x64 (two per SIMD)   */
 };
 
 typedef struct {

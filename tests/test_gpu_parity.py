@@ -22,7 +22,7 @@ if torch.cuda.is_available():
 else:  # collected on CPU-only hosts, never run there
     ts = None
 
-TILES = ["64x64x32", "128x128x64", "256x256x64"]
+TILES = ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"]
 IO = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
 
 
@@ -52,7 +52,8 @@ def assert_accept(c_gpu, C, S, c_dtype, what=""):
 
 # ---- exactness with integer inputs ---------------------------------------------------
 
-SHAPES = {"64x64x32": (200, 300, 130), "128x128x64": (300, 390, 200), "256x256x64": (600, 700, 260)}
+SHAPES = {"64x64x32": (200, 300, 130), "128x128x64": (300, 390, 200), "256x256x64": (600, 700, 260),
+          "256x256x64w8": (600, 700, 260)}
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -72,7 +73,7 @@ def test_integer_inputs_bit_exact(tile, ab, c_dtype):
 @pytest.mark.parametrize("tile", TILES)
 def test_aligned_integer_inputs_bit_exact(tile):
     # whole tiles: the unmasked kernels
-    bm, bn, bk = (int(v) for v in tile.split("x"))
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
     M, N, K = 2 * bm, 3 * bn, 4 * bk
     A, B = workloads.pair(M, N, K, "f16", "int", 501)
     C, _ = og.gemm(A, B, "f16")
@@ -100,7 +101,7 @@ def test_square_256_f16_f32_full_oracle():
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("ab,c_dtype", IO)
 def test_ragged_every_schedule(tile, ab, c_dtype):
-    bm, bn, bk = (int(v) for v in tile.split("x"))
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
     M, N, K = 3 * bm + 17, 4 * bn + 9, 5 * bk + 11   # several tiles and a ragged tail in M, N, K
     A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 600)
     C, S = og.gemm(A, B, ab, threads=4)
@@ -125,7 +126,10 @@ def test_ragged_bf16_5000x12290x1000_full_size():
                   ts.Schedule(order="grouped", group_m=8, tile="256x256x64"),
                   ts.Schedule(order="grouped", group_m=8, mode="persistent", tile="256x256x64"),
                   ts.Schedule(order="grouped", group_m=8, mode="crosstile", xcd_remap=True, tile="256x256x64"),
-                  ts.Schedule(order="grouped", group_m=16, mode="persistent", xcd_remap=True, tile="256x256x64")]:
+                  ts.Schedule(order="grouped", group_m=16, mode="persistent", xcd_remap=True, tile="256x256x64"),
+                  # 8 waves: same per-element accumulation order, so bit-identical too
+                  ts.Schedule(order="grouped", group_m=8, mode="tiled", xcd_remap=True, tile="256x256x64w8"),
+                  ts.Schedule(order="grouped", group_m=8, mode="crosstile", tile="256x256x64w8")]:
         q = ts.query(w.M, w.N, w.K, sched, ts.TS_BF16, ts.TS_F32)
         assert q["masked"] == 1 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
         c = run(A, B, w.ab_dtype, w.c_dtype, sched, w.M, w.N, w.K)

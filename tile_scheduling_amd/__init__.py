@@ -32,7 +32,7 @@ TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_ALIGNMENT, TS_ERR_HIP, TS_
 TS_F16, TS_BF16, TS_F32 = 1, 2, 3
 ORDERS = {"row_major": 0, "grouped": 1}
 MODES = {"tiled": 0, "persistent": 1, "crosstile": 2}
-TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3}
+TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3, "256x256x64w8": 4}
 
 
 class _Schedule(ctypes.Structure):
@@ -84,7 +84,7 @@ class Schedule:
     mode: str = "tiled"           # "tiled" | "persistent" | "crosstile"
     num_programs: int = 0         # persistent grid; 0 = CUs x workgroups per CU
     xcd_remap: bool = False       # contiguous tile-id runs per XCD
-    tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64"
+    tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64" | "256x256x64w8"
 
     def _c(self) -> _Schedule:
         return _Schedule(ORDERS[self.order], int(self.group_m), MODES[self.mode],

@@ -67,6 +67,7 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
     switch (cfg) {
         case CFG_64: *bm = Cfg64::BM; *bn = Cfg64::BN; *bk = Cfg64::BK; break;
         case CFG_128: *bm = Cfg128::BM; *bn = Cfg128::BN; *bk = Cfg128::BK; break;
+        case CFG_256W8: *bm = Cfg256w8::BM; *bn = Cfg256w8::BN; *bk = Cfg256w8::BK; break;
         default: *bm = Cfg256::BM; *bn = Cfg256::BN; *bk = Cfg256::BK; break;
     }
 }
@@ -75,6 +76,7 @@ KernelRef kernel_of(const Plan& p) {
     switch (p.cfg) {
         case CFG_64: return kernels_cfg64(p.io, p.masked, p.mode);
         case CFG_128: return kernels_cfg128(p.io, p.masked, p.mode);
+        case CFG_256W8: return kernels_cfg256w8(p.io, p.masked, p.mode);
         default: return kernels_cfg256(p.io, p.masked, p.mode);
     }
 }
@@ -104,12 +106,13 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
         return TS_ERR_INVALID_ARG;
     if (s.num_programs < 0) return TS_ERR_INVALID_ARG;
     if (s.xcd_remap != 0 && s.xcd_remap != 1) return TS_ERR_INVALID_ARG;
-    if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64) return TS_ERR_INVALID_ARG;
+    if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64_W8) return TS_ERR_INVALID_ARG;
 
     int cfg = s.tile_config;
     if (cfg == TS_TILE_AUTO) {
-        // largest tile that still gives the chip at least half a wave of tiles
-        if (cdiv64(M, 256) * cdiv64(N, 256) >= 128) cfg = CFG_256;
+        // largest tile that still gives the chip at least half a wave of tiles;
+        // 256x256 tiles run with 8 waves (two per SIMD hide each other's stalls)
+        if (cdiv64(M, 256) * cdiv64(N, 256) >= 128) cfg = CFG_256W8;
         else if (cdiv64(M, 128) * cdiv64(N, 128) >= 128) cfg = CFG_128;
         else cfg = CFG_64;
     }

@@ -87,7 +87,7 @@ struct TileCfg {
     static constexpr int A_SLOT = BM * ROW_BYTES, B_SLOT = BN * ROW_BYTES;
     static constexpr int B_BASE = 2 * A_SLOT;           // LDS: [A0][A1][B0][B1]
     static constexpr int LDS_BYTES = 2 * (A_SLOT + B_SLOT);
-    static constexpr int HOLD = (FM * FN >= 8) ? 8 : FM * FN / 2;  // MFMAs issued after the barrier
+    static constexpr int HOLD = (FM * FN >= 16) ? 8 : FM * FN / 2;  // MFMAs issued after the barrier
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tile must be whole 32x32 blocks");
     static_assert(BK % 16 == 0 && KCH <= 8 && (KCH & (KCH - 1)) == 0, "BK must be 16, 32 or 64");
     static_assert(BK % KBH == 0 && NT % KCH == 0, "loader shape");
@@ -242,8 +242,9 @@ struct Engine {
         }
         if (A_DMA) {
             // lane l of a 1 KiB load lands at row (8 * grp + l/8), chunk l%8 of the
-            // slot and fetches the logical chunk the swizzle puts there; grp mod 8
-            // = 4 * (c mod 2) + wave, so even and odd loads c differ in chunk bit 2
+            // slot and fetches the logical chunk the swizzle puts there; with
+            // grp = c * NW + wave, grp mod 8 depends on c only through bit 2 of
+            // c * NW (4 waves: even and odd c differ; 8 waves: never)
             const int row = lane >> 3, pc = lane & 7;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -321,7 +322,7 @@ struct Engine {
             const int soff = (int)((long long)grp * 8 * g.lda * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (__attribute__((address_space(3))) void*)(lds + SLOT * Cfg::A_SLOT + grp * 1024), 16,
-                (int)a_go[c & 1], soff, 0, 0);
+                (int)a_go[((c * NW) >> 2) & 1], soff, 0, 0);
         }
     }
 
@@ -480,11 +481,44 @@ struct Engine {
         bool vb;
     };
 
-    // Sub-step S of a K step on slot SLOT.  On the unmasked path every MFMA slot
-    // carries at most one fragment read for the next sub-step plus one global load
-    // (sub-step 0) or one LDS write (store sub-steps), in a fixed order enforced by
-    // scheduling barriers, so that no burst of memory instructions stalls the
-    // wave's issue while the matrix unit has nothing queued.
+    // Issue plan of the unmasked path over the MFMA slots of a K step (global slot
+    // index gt = S * NMF + t): the VMEM loads and the B writes into LDS are spread
+    // over the whole step, one per few MFMAs, so that neither the texture path nor
+    // the LDS ever backs up far enough to stall the wave's in-order issue while
+    // the matrix unit waits; each slot also carries at most one fragment read for
+    // the next sub-step.  Loads must all be issued before the B writes start.
+    static constexpr int NVM = KBH + (A_DMA ? A_DMA_N : CA);   // VMEM loads per step
+    static constexpr int NSLOT = SUB * NMF - Cfg::HOLD;       // MFMA slots before the barrier
+    // Small tiles have too few MFMA slots: all loads at slot 0, all B writes after
+    // the last sub-step's MFMAs.
+    static constexpr bool SPREAD = NSLOT >= NVM + 8;
+    static constexpr int VM_STRIDE = NSLOT >= 3 * (NVM + 8) ? 3 : (NSLOT >= 2 * (NVM + 8) ? 2 : 1);
+    static constexpr int VM_FIRST = 1;                                       // loads at VM_FIRST + i*VM_STRIDE
+    static constexpr int ST_FIRST = SPREAD ? VM_FIRST + NVM * VM_STRIDE : 1 << 20;  // B writes at ST_FIRST + j*VM_STRIDE
+
+    template <int SLOT>
+    __device__ __forceinline__ void issue_load(int vi, const __amdgpu_buffer_rsrc_t& ra_rsrc,
+                                               const __amdgpu_buffer_rsrc_t& rb_rsrc, int bset) {
+        if (vi < KBH) {
+            const int soff = (int)(vi * g.ldb * 2);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                rb_rsrc, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
+            if (bset == 0) rb[0][vi] = v; else rb[B_DIST - 1][vi] = v;
+        } else if (A_DMA) {
+            const int c = vi - KBH;
+            const int grp = c * NW + wave;
+            const int soff = (int)((long long)grp * 8 * g.lda * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra_rsrc, (__attribute__((address_space(3))) void*)(lds + (SLOT ^ 1) * Cfg::A_SLOT + grp * 1024),
+                16, (int)a_go[((c * NW) >> 2) & 1], soff, 0, 0);
+        } else {
+            const int c = vi - KBH;
+            const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
+            ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)a_go[0], soff, 0);
+        }
+    }
+
+    // Sub-step S of a K step on slot SLOT.
     template <int SLOT, int S>
     __device__ __forceinline__ void substep(const Next& nx) {
         constexpr int b = S & 1;
@@ -505,41 +539,35 @@ struct Engine {
             __builtin_amdgcn_sched_barrier(0);
             return;
         }
-        // unmasked: resources and scalar offsets first
-        __amdgpu_buffer_rsrc_t rb_rsrc, ra_rsrc;
-        if (S == 0) {
-            rb_rsrc = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
-            ra_rsrc = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
-        }
-        constexpr int NVM = KBH + (A_DMA ? A_DMA_N : CA);
+        const __amdgpu_buffer_rsrc_t rb_rsrc = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+        const __amdgpu_buffer_rsrc_t ra_rsrc = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+        constexpr int NT_ = (nmf > NFR ? nmf : NFR);
 #pragma unroll
-        for (int t = 0; t < (nmf > NFR ? nmf : NFR); ++t) {
+        for (int t = 0; t < NT_; ++t) {
+            const int gt = S * NMF + t;
             if (t < nmf) mfma_one(b, t);
             if (t < NFR) read_frag<SLOT>(S + 1 < SUB ? S + 1 : 0, t, b ^ 1);
-            if (S == 0 && t < NVM) {
-                if (t < KBH) {
-                    const int soff = (int)(t * g.ldb * 2);
-                    rb[BSET][t] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rb_rsrc, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
-                } else if (A_DMA) {
-                    const int c = t - KBH;
-                    const int grp = c * NW + wave;
-                    const int soff = (int)((long long)grp * 8 * g.lda * 2);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        ra_rsrc, (__attribute__((address_space(3))) void*)(lds + (SLOT ^ 1) * Cfg::A_SLOT + grp * 1024),
-                        16, (int)a_go[c & 1], soff, 0, 0);
-                } else {
-                    const int c = t - KBH;
-                    const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
-                    ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)a_go[0], soff, 0);
-                }
+            if (SPREAD) {
+                const int vi = (gt - VM_FIRST) / VM_STRIDE;  // load number at this slot
+                if (gt >= VM_FIRST && (gt - VM_FIRST) % VM_STRIDE == 0 && vi < NVM)
+                    issue_load<SLOT>(vi, ra_rsrc, rb_rsrc, BSET);
+            } else if (gt == 0) {
+#pragma unroll
+                for (int vi = 0; vi < NVM; ++vi) issue_load<SLOT>(vi, ra_rsrc, rb_rsrc, BSET);
             }
-            if (S == B_STORE_S && t < 8) store_b_one<BSTORE, SLOT ^ 1>(t);
+            const int wi = (gt - ST_FIRST) / VM_STRIDE;  // B write number at this slot
+            if (gt >= ST_FIRST && (gt - ST_FIRST) % VM_STRIDE == 0 && wi < 8) store_b_one<BSTORE, SLOT ^ 1>(wi);
             if (!A_DMA && S == A_STORE_S && t < CA) {
                 if (Cfg::NA % NT == 0 || t * NT + tid < Cfg::NA)
                     *reinterpret_cast<u32x4*>(lds + (SLOT ^ 1) * Cfg::A_SLOT + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[0][t];
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // B writes that did not fit before the barrier slots
+        if (last) {
+#pragma unroll
+            for (int wj = 0; wj < 8; ++wj)
+                if (ST_FIRST + wj * VM_STRIDE >= S * NMF + NT_) store_b_one<BSTORE, SLOT ^ 1>(wj);
         }
     }
 

@@ -11,11 +11,12 @@ namespace ts {
 enum : int { IO_F16_F16 = 0, IO_F16_F32 = 1, IO_BF16_BF16 = 2, IO_BF16_F32 = 3 };
 
 // Tile configurations (same numbering as TS_TILE_* in tsgemm.h).
-enum : int { CFG_64 = 1, CFG_128 = 2, CFG_256 = 3 };
+enum : int { CFG_64 = 1, CFG_128 = 2, CFG_256 = 3, CFG_256W8 = 4 };
 
 typedef TileCfg<64, 64, 32, 2, 2> Cfg64;
 typedef TileCfg<128, 128, 64, 2, 2> Cfg128;
 typedef TileCfg<256, 256, 64, 2, 2> Cfg256;
+typedef TileCfg<256, 256, 64, 2, 4> Cfg256w8;   // 8 waves: two per SIMD
 
 struct KernelRef {
     const void* fn;  // __global__ function, launched with one GemmArgs argument
@@ -48,5 +49,6 @@ KernelRef kernel_for(int io, bool masked, int mode) {
 KernelRef kernels_cfg64(int io, bool masked, int mode);
 KernelRef kernels_cfg128(int io, bool masked, int mode);
 KernelRef kernels_cfg256(int io, bool masked, int mode);
+KernelRef kernels_cfg256w8(int io, bool masked, int mode);
 
 }  // namespace ts
