@@ -52,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct InF16 {};
 struct InBF16 {};
@@ -85,8 +86,11 @@ struct TileCfg {
     static constexpr int CB = (NB + NT - 1) / NT;       // B blocks per thread
     static constexpr int ROW_BYTES = BK * 2;            // one LDS row (m or n) of a slice
     static constexpr int A_SLOT = BM * ROW_BYTES, B_SLOT = BN * ROW_BYTES;
-    static constexpr int B_BASE = 2 * A_SLOT;           // LDS: [A0][A1][B0][B1]
-    static constexpr int LDS_BYTES = 2 * (A_SLOT + B_SLOT);
+    // LDS: A slots [A0][A1]([A2]) and B slots [B0][B1] (two arrays); BK = 64 tiles
+    // get a third A slot when it fits
+    static constexpr int A_RING = (BK == 64 && 3 * A_SLOT + 2 * B_SLOT <= 160 * 1024) ? 3 : 2;
+    static constexpr int A_BYTES = A_RING * A_SLOT, B_BYTES = 2 * B_SLOT;
+    static constexpr int LDS_BYTES = A_BYTES + B_BYTES;
     static constexpr int HOLD = (FM * FN >= 16) ? 8 : FM * FN / 2;  // MFMAs issued after the barrier
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tile must be whole 32x32 blocks");
     static_assert(BK % 16 == 0 && KCH <= 8 && (KCH & (KCH - 1)) == 0, "BK must be 16, 32 or 64");
@@ -175,15 +179,35 @@ __device__ __forceinline__ u32x4 lds_read16(const char* lds, uint32_t off) {
     return *reinterpret_cast<const u32x4*>(lds + off);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16).  Each lane addresses 4 consecutive
+// 16-bit elements; within every group of 16 lanes, lane 4a + c receives element
+// c of the chunks addressed by lanes a, a + 4, a + 8 and a + 12.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) i16x4*)(lds + off)));
+}
+
 // ---- the tile engine -------------------------------------------------------------
 
-// Pipelines (per K step of 64 MFMAs per wave on LDS slot SLOT):
-//  fast (unmasked, BK = 64): A arrives by direct-to-LDS buffer loads issued at
-//    sub-step 0 into slot SLOT^1 (one slice ahead); B travels two slices ahead in
-//    registers and is transposed into slot SLOT^1 at sub-step 1.  Before the
-//    step's barrier each wave waits for its own loads.
+// Two pipelines feed the MFMAs of a K step (64 MFMAs per wave for the big tiles):
+//
+//  fast (unmasked, BK = 64, 128- or 256-wide tiles).  Both operands go straight
+//    from global memory into LDS with direct-to-LDS buffer loads, no registers
+//    in between:
+//      A ([m][k], 16-byte chunks swizzled by swz(r) below) into a ring of three
+//        slots, two slices ahead of the slice being multiplied;
+//      B in the slice's natural [k][n] layout (chunks swizzled by f(k) below)
+//        into two slots, one slice ahead, read back as MFMA operands with LDS
+//        transpose reads.
+//    A step issues B first, then A; it ends with each wave waiting for all but
+//    its A loads of this step, then the workgroup barrier.  The 3 + 2 slots of
+//    256 x 64 slices fill the 160 KiB of LDS exactly.  The loads are issued as
+//    inline assembly: the compiler then neither waits for them before LDS reads
+//    it cannot prove disjoint (the ring slot is chosen at run time) nor counts
+//    them, and the one wait the pipeline needs is explicit.
 //  register (masked edges, or BK = 32): A and B one slice ahead in registers,
-//    written into slot SLOT^1 at the last sub-steps.
+//    written at the last sub-steps into the other slot of two; B is transposed to
+//    [n][k] with byte permutes on the way in.
 template <class Cfg, class TI, class TO, bool MASKED>
 struct Engine {
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
@@ -194,55 +218,73 @@ struct Engine {
     static constexpr int NMF = FM * FN;              // MFMAs per sub-step
     static constexpr int A_ROWS_PER_C = NT / KCH;    // A rows between a thread's chunks
     static constexpr int NBN = BN / 8;               // B loader blocks along n
-    static constexpr bool A_DMA = !MASKED && RB == 128 && (BM * RB) % (1024 * NW) == 0;
-    static constexpr int A_DMA_N = A_DMA ? BM * RB / 1024 / NW : 0;  // 1 KiB DMA loads per wave
-    static constexpr int B_DIST = A_DMA ? 2 : 1;     // B slices in flight in registers
-    static constexpr int A_SETS = A_DMA ? 0 : 1;
-    // sub-steps that write the next slice into LDS
-    static constexpr int A_STORE_S = SUB > 2 ? SUB - 2 : SUB - 1;       // register path only
-    static constexpr int B_STORE_S = A_DMA ? (SUB > 1 ? 1 : 0) : SUB - 1;
+    static constexpr int RBB = BN * 2;               // bytes of one [k][n] B row (fast path)
+    static constexpr int LPR = RBB / 16, RPD = 64 / LPR;   // B load lanes per row, rows per 1 KiB load
+    static constexpr bool FAST = !MASKED && RB == 128 && Cfg::A_RING == 3 && (BM * RB) % (1024 * NW) == 0 &&
+                                 LPR >= 16 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
+                                 (BK * RBB) % (1024 * NW) == 0 && (NW * RPD) % 8 == 0;
+    static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
+    static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
+    static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
+    static constexpr int NJB = FN < 4 ? FN : 4;      // per-lane B transpose-read offsets
+    // sub-steps that write the next slice into LDS (register path)
+    static constexpr int A_STORE_S = SUB > 2 ? SUB - 2 : SUB - 1;
+    static constexpr int B_STORE_S = SUB - 1;
     static_assert(CB == 1, "one B loader block per thread");
 
     const GemmArgs& g;
-    char* lds;
+    char* lds;            // A slots
+    char* ldsb;           // B slots
     int tid, lane, wm, wn, wave;
+    int as_cur;           // fast path: A ring slot of the slice being multiplied
 
     // per-lane LDS byte offsets
-    uint32_t a_rd[SUB];   // fragment read of block 0 at sub-step s (block i: + i*32*RB)
-    uint32_t b_rd[SUB];
-    uint32_t a_wr[2];     // A chunk c (register path): a_wr[c&1] + c*A_ROWS_PER_C*RB
-    uint32_t b_wr[8];     // B write j of the loader block
-    uint32_t b_sel[2];    // byte-permute selector of B writes with even / odd j
+    uint32_t a_rd[SUB];   // A fragment read of block 0 at sub-step s (block i: + i*32*RB);
+                          // fast path: includes the current ring slot
+    uint32_t b_rd[SUB];   // register path: B fragment read, as a_rd
+    uint32_t bt_rd[NJB];  // fast path: B transpose read of block u (block j: bt_rd[j % 4] + (j / 4) * 256)
+    uint32_t b_dg[2];     // fast path: B load global offset, by bit 3 of its first row
+    uint32_t lds_a_at, lds_b_at;  // LDS addresses of the A and B slots
+    uint32_t a_wr[2];     // register path: A chunk c at a_wr[c&1] + c*A_ROWS_PER_C*RB
+    uint32_t b_wr[8];     // B write j of the loader block (see b_wr_at)
+    uint32_t b_sel[2];    // register path: byte-permute selector of B writes with even / odd j
     // per-lane global byte offsets
     uint32_t a_go[2], b_go;   // A: [c&1] of the load / chunk index c
     bool b_active;        // this thread owns a B loader block
 
-    u32x4 ra[A_SETS > 0 ? A_SETS : 1][CA];   // A slice in flight (register path)
-    u32x4 rb[B_DIST][KBH];                   // B slices in flight (KBH rows of 8 columns)
+    u32x4 ra[FAST ? 1 : CA];                 // A slice in flight (register path)
+    u32x4 rb[1][KBH];                        // B slice in flight (register path; KBH rows of 8 columns)
     u32x4 fa[2][FM], fb[2][FN];
     f32x16 acc[FM][FN];
 
-    __device__ __forceinline__ Engine(const GemmArgs& g_, char* lds_) : g(g_), lds(lds_) {
+    __device__ __forceinline__ Engine(const GemmArgs& g_, char* lds_a, char* lds_b) : g(g_), lds(lds_a), ldsb(lds_b) {
         tid = threadIdx.x;
         lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         wm = wave / Cfg::WN;
         wn = wave % Cfg::WN;
+        as_cur = 0;
+        lds_a_at = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_a;
+        lds_b_at = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_b;
         const int r32 = lane & 31, hk = lane >> 5;
-        // Rows of both operands are swizzled by swz(r) = (r ^ (r >> 3)) mod KCH.  A
-        // fragment row is (32-aligned base) + r32, so swz depends on r32 and, for
-        // KCH = 8, on bit 0 of the block index (bit 5 of the row), which flips chunk
-        // bit 2, i.e. sub-step s <-> s ^ 2: odd blocks use the offset of s ^ 2.
+        // Rows of [m][k] (and, on the register path, [n][k]) slices are swizzled by
+        // swz(r) = (r ^ (r >> 3)) mod KCH.  A fragment row is (32-aligned base) +
+        // r32, so swz depends on r32 and, for KCH = 8, on bit 0 of the block index
+        // (bit 5 of the row), which flips chunk bit 2, i.e. sub-step s <-> s ^ 2:
+        // odd blocks use the offset of s ^ 2.
         const int sw = (r32 ^ (r32 >> 3)) & (KCH - 1);
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             const int ch = 2 * s + hk;
             a_rd[s] = (uint32_t)((wm * Cfg::TM + r32) * RB + ((ch ^ sw) * 16));
-            b_rd[s] = (uint32_t)(Cfg::B_BASE + (wn * Cfg::TN + r32) * RB + ((ch ^ sw) * 16));
+            b_rd[s] = (uint32_t)((wn * Cfg::TN + r32) * RB + ((ch ^ sw) * 16));
         }
-        if (A_DMA) {
-            // lane l of a 1 KiB load lands at row (8 * grp + l/8), chunk l%8 of the
-            // slot and fetches the logical chunk the swizzle puts there; with
+        const int nb = tid % NBN, kb = tid / NBN;   // B loader block (kb, nb) of this thread
+        b_active = Cfg::NB % NT == 0 || tid < Cfg::NB;
+        b_go = (uint32_t)(((long long)kb * KBH * g.ldb + nb * 8) * 2);
+        if (FAST) {
+            // A: lane l of a 1 KiB load lands at row (8 * grp + l/8), chunk l%8 of
+            // the slot and fetches the logical chunk the swizzle puts there; with
             // grp = c * NW + wave, grp mod 8 depends on c only through bit 2 of
             // c * NW (4 waves: even and odd c differ; 8 waves: never)
             const int row = lane >> 3, pc = lane & 7;
@@ -252,6 +294,37 @@ struct Engine {
                 a_go[e] = (uint32_t)(((long long)row * g.lda + ((pc ^ row ^ grp7) * 8)) * 2);
                 a_wr[e] = 0;
             }
+            // B: [k][n] rows whose 16-byte chunks are XOR-swizzled by
+            //   f(k) = 4 (k mod 4) ^ 2 (bit 3 of k),
+            // so that the 4 k rows x 64 bytes that 32 lanes of a transpose read
+            // touch (and the 8 rows x 32 bytes of lanes 0-15 with 32-47) fall in
+            // distinct banks.  Transpose read: lane j of 16-lane group q addresses
+            // row 16 s + 8 hk + 4 rd + j/4 (hk = q/2), columns 16 (q mod 2) +
+            // 4 (j mod 4) of its 32-column block, so that lane 16 q + i ends up with
+            // 4 consecutive k of column i + 16 (q mod 2); two reads (rd = 0, 1) make
+            // the 8 k values of its MFMA operand.  There k mod 4 = j/4 and bit 3 of
+            // k = hk, so the swizzle is fixed per lane.
+            const int q = lane >> 4, j = lane & 15;
+            const int qh = q >> 1, qn = q & 1, e = j >> 2, a = j & 3;
+            const int ff = (4 * e) ^ (2 * qh);
+#pragma unroll
+            for (int u = 0; u < NJB; ++u) {
+                const int W = wn * FN + u;   // 32-column block within the tile
+                const int chunk = ((4 * W) | (2 * qn + (a >> 1))) ^ ff;
+                bt_rd[u] = (uint32_t)((8 * qh + e) * RBB + chunk * 16 + (a & 1) * 8);
+            }
+            // B loads: lane l lands at row RPD * grp + l / LPR, chunk l mod LPR, and
+            // fetches the logical chunk the swizzle puts there; bit 3 of the row
+            // varies with the load index c through c * NW * RPD (a multiple of 8)
+            const int rl = lane / LPR, pch = lane % LPR;
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const int r = 8 * e2 + wave * RPD + rl;
+                const int fr = (4 * (r & 3)) ^ (2 * ((r >> 3) & 1));
+                b_dg[e2] = (uint32_t)(((long long)rl * g.ldb + (pch ^ fr) * 8) * 2);
+            }
+            b_wr[0] = 0;
+            b_sel[0] = b_sel[1] = 0;
         } else {
             // A chunk (row, kc) of this thread; chunk c adds c * A_ROWS_PER_C rows,
             // which changes the swizzle only through bit 2 for odd c (KCH = 8)
@@ -262,38 +335,57 @@ struct Engine {
                 a_wr[e] = (uint32_t)(r * RB + ((kc ^ ((r ^ (r >> 3)) & (KCH - 1))) * 16)) - e * A_ROWS_PER_C * RB;
                 a_go[e] = (uint32_t)(((long long)row * g.lda + kc * 8) * 2);
             }
-        }
-        {   // B loader block (kb, nb) of this thread.  Write instruction j of lane
-            // group half h = (nb >> 3) & 1 stores column j ^ h, so that the 16 lanes
-            // served together cover both row parities and 16 distinct bank groups.
-            const int nb = tid % NBN, kb = tid / NBN;
+            // B is transposed to [n][k]: write instruction j of lane group half
+            // h = (nb >> 3) & 1 stores column j ^ h, so that the 16 lanes served
+            // together cover both row parities and 16 distinct bank groups.  Its
+            // LDS row is n = 8 nb + (j ^ h) and its chunk (c0 ^ swz(n)) with
+            // swz(n) = (j ^ h ^ nb) mod 8; with 128-byte rows the offset is
+            //   base + ((j ^ h) * 128) + ((x ^ j) * 16),  x = (c0 ^ h ^ nb) mod 8,
+            // whose variable bits 4..9 sit above and apart from base's, so it equals
+            // b_wr ^ (j * 144) with b_wr = base | (h * 128) | (x * 16).
             const int h = (nb >> 3) & 1;
-            b_active = Cfg::NB % NT == 0 || tid < Cfg::NB;
             b_sel[0] = h ? 0x07060302u : 0x05040100u;   // even j: half (j ^ h) & 1
             b_sel[1] = h ? 0x05040100u : 0x07060302u;   // odd j
+            if (KCH == 8) {
+                const int c0 = KBH == 8 ? kb : (kb >> 1);
+                const int x = (c0 ^ h ^ nb) & 7;
+                const uint32_t base = (uint32_t)(nb * 8 * RB + (KBH == 8 ? 0 : (kb & 1) * 8));
+                b_wr[0] = base | (uint32_t)(h * 128) | (uint32_t)(x * 16);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int n = nb * 8 + (j ^ h);
-                const int swz = (n ^ (n >> 3)) & (KCH - 1);
-                if (KBH == 8)
-                    b_wr[j] = (uint32_t)(Cfg::B_BASE + n * RB + ((kb ^ swz) * 16));
-                else
-                    b_wr[j] = (uint32_t)(Cfg::B_BASE + n * RB + ((((kb >> 1) ^ swz)) * 16) + (kb & 1) * 8);
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int n = nb * 8 + (jj ^ h);
+                    const int swz = (n ^ (n >> 3)) & (KCH - 1);
+                    if (KBH == 8)
+                        b_wr[jj] = (uint32_t)(n * RB + ((kb ^ swz) * 16));
+                    else
+                        b_wr[jj] = (uint32_t)(n * RB + ((((kb >> 1) ^ swz)) * 16) + (kb & 1) * 8);
+                }
             }
-            b_go = (uint32_t)(((long long)kb * KBH * g.ldb + nb * 8) * 2);
         }
         // Keep the lane offsets opaque: otherwise their compile-time parts (the B
-        // region starts at 64 KiB) are folded into per-access constants too large
-        // for the 16-bit LDS offset field, and every access needs its own register.
+        // region starts at 64 KiB or more) are folded into per-access constants too
+        // large for the 16-bit LDS offset field, and every access needs its own
+        // register.
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             asm volatile("" : "+v"(a_rd[s]));
-            asm volatile("" : "+v"(b_rd[s]));
+            if (!FAST) asm volatile("" : "+v"(b_rd[s]));
         }
-        asm volatile("" : "+v"(a_wr[0]));
-        asm volatile("" : "+v"(a_wr[1]));
+        if (FAST) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(b_wr[j]));
+            for (int u = 0; u < NJB; ++u) asm volatile("" : "+v"(bt_rd[u]));
+        } else {
+            asm volatile("" : "+v"(a_wr[0]));
+            asm volatile("" : "+v"(a_wr[1]));
+        }
+        if (FAST) {
+        } else if (KCH == 8) {
+            asm volatile("" : "+v"(b_wr[0]));
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+v"(b_wr[jj]));
+        }
     }
 
     __device__ __forceinline__ void zero_acc() {
@@ -312,18 +404,58 @@ struct Engine {
                                                  __builtin_amdgcn_readfirstlane(valid ? -1 : 0), kBufferFlags);
     }
 
-    // A slice k of tile row m0 straight into LDS slot SLOT (fast path).
-    template <int SLOT>
-    __device__ __forceinline__ void dma_a(int m0, int k, bool valid) {
-        const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
+    // Fast path: ring slot after / two after slot `s`.
+    static __device__ __forceinline__ int ring1(int s) { return s == 2 ? 0 : s + 1; }
+    static __device__ __forceinline__ int ring2(int s) { return s == 0 ? 2 : s - 1; }
+
+    // Fast path: buffer resource as four scalar registers, for inline assembly.
+    __device__ __forceinline__ u32x4 srsrc(const uint16_t* p, bool valid) const {
+        const uint64_t a = (uint64_t)(uintptr_t)p;
+        u32x4 r;
+        r[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        r[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+        r[2] = (uint32_t)__builtin_amdgcn_readfirstlane(valid ? -1 : 0);
+        r[3] = (uint32_t)kBufferFlags;
+        return r;
+    }
+
+    // Fast path: one direct-to-LDS load of 16 bytes per lane; lane l's bytes land at
+    // LDS address m0 + 16 l.  The M0 write needs one wait state before the load.
+    static __device__ __forceinline__ void dma16(const u32x4& r, uint32_t voff, int soff, uint32_t m0) {
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     ::"s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+    }
+
+    // Fast path: 1 KiB A load number c of this wave, into ring slot `slot`.
+    __device__ __forceinline__ void dma_a_one(int slot, int c, const u32x4& r) {
+        const int grp = c * NW + wave;                     // 8-row group (1 KiB)
+        dma16(r, a_go[((c * NW) >> 2) & 1], (int)((long long)grp * 8 * g.lda * 2),
+              lds_a_at + (uint32_t)(slot * Cfg::A_SLOT + grp * 1024));
+    }
+    __device__ __forceinline__ void dma_a(int slot, int m0, int k, bool valid) {
+        const u32x4 r = srsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
 #pragma unroll
-        for (int c = 0; c < A_DMA_N; ++c) {
-            const int grp = c * NW + wave;                     // 8-row group (1 KiB)
-            const int soff = (int)((long long)grp * 8 * g.lda * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(lds + SLOT * Cfg::A_SLOT + grp * 1024), 16,
-                (int)a_go[((c * NW) >> 2) & 1], soff, 0, 0);
-        }
+        for (int c = 0; c < A_DMA_N; ++c) dma_a_one(slot, c, r);
+    }
+    // Fast path: 1 KiB B load number c of this wave, into B slot `slot`.
+    __device__ __forceinline__ void dma_b_one(int slot, int c, const u32x4& r) {
+        const int grp = c * NW + wave;                     // RPD-row group (1 KiB)
+        dma16(r, b_dg[((c * NW * RPD) >> 3) & 1], (int)((long long)grp * RPD * g.ldb * 2),
+              lds_b_at + (uint32_t)(slot * Cfg::B_SLOT + grp * 1024));
+    }
+    __device__ __forceinline__ void dma_b(int slot, int n0, int k, bool valid) {
+        const u32x4 r = srsrc(g.B + (long long)k * BK * g.ldb + n0, valid);
+#pragma unroll
+        for (int c = 0; c < B_DMA_N; ++c) dma_b_one(slot, c, r);
+    }
+
+    // Fast path: next ring slot; the A read offsets follow it.
+    __device__ __forceinline__ void advance_a() {
+        const bool wrap = as_cur == 2;
+        as_cur = wrap ? 0 : as_cur + 1;
+        const uint32_t d = wrap ? (uint32_t)(-2 * Cfg::A_SLOT) : (uint32_t)Cfg::A_SLOT;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) a_rd[s] += d;
     }
 
     // A slice k of tile row m0 into registers (register path).
@@ -334,7 +466,7 @@ struct Engine {
 #pragma unroll
             for (int c = 0; c < CA; ++c) {
                 const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
-                ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)a_go[0], soff, 0);
+                ra[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)a_go[0], soff, 0);
             }
             return;
         }
@@ -345,8 +477,17 @@ struct Engine {
             const int gm = m0 + row, gk = k0 + kc * 8;
             const uint16_t* p = g.A + (long long)gm * g.lda + gk;
             const bool in = valid && (Cfg::NA % NT == 0 || idx < Cfg::NA) && gm < g.M;
-            ra[0][c] = in ? load8_masked(p, g.K - gk, g.vec_a) : u32x4{0, 0, 0, 0};
+            ra[c] = in ? load8_masked(p, g.K - gk, g.vec_a) : u32x4{0, 0, 0, 0};
         }
+    }
+
+    // B row q of slice k, tile column n0, into register set SET (unmasked).
+    template <int SET>
+    __device__ __forceinline__ void load_b_row(int q, const __amdgpu_buffer_rsrc_t& r) {
+        const int soff = (int)(q * g.ldb * 2);
+        // threads without a B block re-read thread 0's block (in bounds); the value
+        // is never stored
+        rb[SET][q] = __builtin_amdgcn_raw_buffer_load_b128(r, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
     }
 
     // B slice k of tile column n0 into register set SET.
@@ -356,13 +497,7 @@ struct Engine {
         if (!MASKED) {
             const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k0 * g.ldb + n0, valid);
 #pragma unroll
-            for (int q = 0; q < KBH; ++q) {
-                const int soff = (int)(q * g.ldb * 2);
-                // threads without a B block re-read thread 0's block (in bounds);
-                // the value is never stored
-                rb[SET][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                    r, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
-            }
+            for (int q = 0; q < KBH; ++q) load_b_row<SET>(q, r);
             return;
         }
         const int nb = tid % NBN, kb = tid / NBN;
@@ -382,77 +517,80 @@ struct Engine {
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             if (Cfg::NA % NT == 0 || c * NT + tid < Cfg::NA)
-                *reinterpret_cast<u32x4*>(sa + a_wr[c & 1] + c * A_ROWS_PER_C * RB) = ra[0][c];
+                *reinterpret_cast<u32x4*>(sa + a_wr[c & 1] + c * A_ROWS_PER_C * RB) = ra[c];
         }
     }
 
-    // Register set SET -> LDS slot SLOT (B part), transposed to [n][k].
-    template <int SET, int SLOT>
-    __device__ __forceinline__ void store_b() {
-        if (!(Cfg::NB % NT == 0) && !b_active) return;
-        char* sb = lds + SLOT * Cfg::B_SLOT;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            // column j ^ h of the block: element j ^ h of every loaded row (both sit
-            // in dword j >> 1; the lane's selector picks the half)
-            const int d = j >> 1;
-            const uint32_t sel = b_sel[j & 1];
-            if (KBH == 8) {
-                u32x4 col;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
-                *reinterpret_cast<u32x4*>(sb + b_wr[j]) = col;
-            } else {
-                u32x2 col;
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
-                *reinterpret_cast<u32x2*>(sb + b_wr[j]) = col;
-            }
-        }
+    // Number of LDS writes of one B slice per thread (register path).
+    static constexpr int NBW = FAST ? 0 : 8;
+
+    // LDS offset of B write j (slot 0).
+    __device__ __forceinline__ uint32_t b_wr_at(int j) const {
+        return KCH == 8 ? (b_wr[0] ^ (uint32_t)(j * 144)) : b_wr[j];
     }
 
-    template <int SLOT>
-    __device__ __forceinline__ void read_frags(int s, int buf) {
-        const char* base_a = lds + SLOT * Cfg::A_SLOT;
-        const char* base_b = lds + SLOT * Cfg::B_SLOT;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = lds_read16(base_a, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = lds_read16(base_b, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
-    }
-
-    // Fragment number idx (A blocks first, then B blocks) of sub-step s.
-    template <int SLOT>
-    __device__ __forceinline__ void read_frag(int s, int idx, int buf) {
-        if (idx < FM) {
-            const int i = idx;
-            fa[buf][i] = lds_read16(lds + SLOT * Cfg::A_SLOT, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
-        } else {
-            const int j = idx - FM;
-            fb[buf][j] = lds_read16(lds + SLOT * Cfg::B_SLOT, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
-        }
-    }
-
-    // Write j of register set SET into B slot SLOT (column j ^ h, see b_wr).
+    // Write j of register set SET into B slot SLOT (register path): column j ^ h
+    // of the loader block (see b_wr), transposed.
     template <int SET, int SLOT>
     __device__ __forceinline__ void store_b_one(int j) {
         if (!(Cfg::NB % NT == 0) && !b_active) return;
-        char* sb = lds + SLOT * Cfg::B_SLOT;
+        char* sb = ldsb + SLOT * Cfg::B_SLOT;
         const int d = j >> 1;
         const uint32_t sel = b_sel[j & 1];
         if (KBH == 8) {
             u32x4 col;
 #pragma unroll
             for (int q = 0; q < 4; ++q) col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
-            *reinterpret_cast<u32x4*>(sb + b_wr[j]) = col;
+            *reinterpret_cast<u32x4*>(sb + b_wr_at(j)) = col;
         } else {
             u32x2 col;
 #pragma unroll
             for (int q = 0; q < 2; ++q) col[q] = __builtin_amdgcn_perm(rb[SET][2 * q + 1][d], rb[SET][2 * q][d], sel);
-            *reinterpret_cast<u32x2*>(sb + b_wr[j]) = col;
+            *reinterpret_cast<u32x2*>(sb + b_wr_at(j)) = col;
         }
+    }
+
+    template <int SET, int SLOT>
+    __device__ __forceinline__ void store_b() {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) store_b_one<SET, SLOT>(j);
+    }
+
+    // A fragment of 32-row block i at sub-step s (A slot SLOT on the register path,
+    // the current ring slot on the fast path).
+    template <int SLOT>
+    __device__ __forceinline__ u32x4 read_a(int s, int i) const {
+        const char* base = lds + (FAST ? 0 : SLOT * Cfg::A_SLOT);
+        return lds_read16(base, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
+    }
+
+    // B fragment of 32-column block j at sub-step s from slot SLOT.
+    template <int SLOT>
+    __device__ __forceinline__ u32x4 read_b(int s, int j) const {
+        if (FAST) {   // two transpose reads: k offsets 0-3 and 4-7 of the lane's half
+            const char* base = ldsb + SLOT * Cfg::B_SLOT + (j >> 2) * 256 + 16 * s * RBB;
+            const u32x2 lo = lds_read_tr(base, bt_rd[j & 3]);
+            const u32x2 hi = lds_read_tr(base + 4 * RBB, bt_rd[j & 3]);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        return lds_read16(ldsb + SLOT * Cfg::B_SLOT, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
+    }
+
+    template <int SLOT>
+    __device__ __forceinline__ void read_frags(int s, int buf) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = read_a<SLOT>(s, i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = read_b<SLOT>(s, j);
+    }
+
+    // Fragment number idx (A blocks first, then B blocks) of sub-step s.
+    template <int SLOT>
+    __device__ __forceinline__ void read_frag(int s, int idx, int buf) {
+        if (idx < FM)
+            fa[buf][idx] = read_a<SLOT>(s, idx);
+        else
+            fb[buf][idx - FM] = read_b<SLOT>(s, idx - FM);
     }
 
     // MFMA number t of a sub-step, in (i, j) order.
@@ -471,9 +609,9 @@ struct Engine {
         }
     }
 
-    // Where the next slices come from: `a` one slice ahead (tile row origin m0,
-    // slice ka), `b` B_DIST slices ahead (tile column origin n0, slice kb).  A
-    // false `*valid` means past the last slice: nothing is read and zeros flow.
+    // Slices loaded by a K step: A slice ka of tile row origin m0 (DA slices ahead
+    // of the one multiplied) and B slice kb of tile column origin n0 (one ahead).
+    // A false `v*` means past the last slice: nothing is read and zeros flow.
     struct Next {
         int m0, ka;
         bool va;
@@ -481,67 +619,88 @@ struct Engine {
         bool vb;
     };
 
-    // Issue plan of the unmasked path over the MFMA slots of a K step (global slot
+    // Issue plan of the unmasked paths over the MFMA slots of a K step (global slot
     // index gt = S * NMF + t): the VMEM loads and the B writes into LDS are spread
     // over the whole step, one per few MFMAs, so that neither the texture path nor
     // the LDS ever backs up far enough to stall the wave's in-order issue while
     // the matrix unit waits; each slot also carries at most one fragment read for
-    // the next sub-step.  Loads must all be issued before the B writes start.
-    static constexpr int NVM = KBH + (A_DMA ? A_DMA_N : CA);   // VMEM loads per step
+    // the next sub-step.  Loads come first (B, then A), then the B writes.
+    static constexpr int NBL = FAST ? B_DMA_N : KBH;           // B loads per step
+    static constexpr int NVM = NBL + (FAST ? A_DMA_N : CA);   // VMEM loads per step
     static constexpr int NSLOT = SUB * NMF - Cfg::HOLD;       // MFMA slots before the barrier
     // Small tiles have too few MFMA slots: all loads at slot 0, all B writes after
     // the last sub-step's MFMAs.
-    static constexpr bool SPREAD = NSLOT >= NVM + 8;
-    static constexpr int VM_STRIDE = NSLOT >= 3 * (NVM + 8) ? 3 : (NSLOT >= 2 * (NVM + 8) ? 2 : 1);
-    static constexpr int VM_FIRST = 1;                                       // loads at VM_FIRST + i*VM_STRIDE
+    static constexpr bool SPREAD = NSLOT >= NVM + NBW;
+    static constexpr int VM_STRIDE = NSLOT >= 3 * (NVM + NBW) ? 3 : (NSLOT >= 2 * (NVM + NBW) ? 2 : 1);
+    static constexpr int VM_FIRST = 1;                                        // loads at VM_FIRST + i*VM_STRIDE
     static constexpr int ST_FIRST = SPREAD ? VM_FIRST + NVM * VM_STRIDE : 1 << 20;  // B writes at ST_FIRST + j*VM_STRIDE
+    static_assert(NVM < 64, "vmcnt range");
 
+    // Fast path: load number vi of a step on B slot SLOT.
     template <int SLOT>
+    __device__ __forceinline__ void issue_dma(int vi, int aslot, const u32x4& ra_, const u32x4& rb_) {
+        if (vi < B_DMA_N)
+            dma_b_one(SLOT ^ 1, vi, rb_);
+        else
+            dma_a_one(aslot, vi - B_DMA_N, ra_);
+    }
+
+    // Register path (unmasked): load number vi of a step.
+    template <int BSET>
     __device__ __forceinline__ void issue_load(int vi, const __amdgpu_buffer_rsrc_t& ra_rsrc,
-                                               const __amdgpu_buffer_rsrc_t& rb_rsrc, int bset) {
+                                               const __amdgpu_buffer_rsrc_t& rb_rsrc) {
         if (vi < KBH) {
-            const int soff = (int)(vi * g.ldb * 2);
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                rb_rsrc, (Cfg::NB % NT == 0 || b_active) ? (int)b_go : 0, soff, 0);
-            if (bset == 0) rb[0][vi] = v; else rb[B_DIST - 1][vi] = v;
-        } else if (A_DMA) {
-            const int c = vi - KBH;
-            const int grp = c * NW + wave;
-            const int soff = (int)((long long)grp * 8 * g.lda * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra_rsrc, (__attribute__((address_space(3))) void*)(lds + (SLOT ^ 1) * Cfg::A_SLOT + grp * 1024),
-                16, (int)a_go[((c * NW) >> 2) & 1], soff, 0, 0);
+            load_b_row<BSET>(vi, rb_rsrc);
         } else {
             const int c = vi - KBH;
             const int soff = (int)(c * A_ROWS_PER_C * g.lda * 2);
-            ra[0][c] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)a_go[0], soff, 0);
+            ra[c] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, (int)a_go[0], soff, 0);
         }
     }
 
-    // Sub-step S of a K step on slot SLOT.
+    // Sub-step S of a K step on B slot SLOT.
     template <int SLOT, int S>
     __device__ __forceinline__ void substep(const Next& nx) {
         constexpr int b = S & 1;
         constexpr bool last = S + 1 == SUB;
         constexpr int nmf = last ? NMF - Cfg::HOLD : NMF;
-        constexpr int BSET = B_DIST == 2 ? SLOT : 0;         // set receiving B loads
-        constexpr int BSTORE = B_DIST == 2 ? (SLOT ^ 1) : 0;  // set written into slot SLOT^1
-        constexpr int NFR = last ? 0 : FM + FN;              // fragment reads to spread
+        constexpr int NFR = last ? 0 : FM + FN;        // fragment reads to spread
         if (MASKED) {
             if (S == 0) {
-                load_b<BSET>(nx.n0, nx.kb, nx.vb);
+                load_b<0>(nx.n0, nx.kb, nx.vb);
                 load_a(nx.m0, nx.ka, nx.va);
             }
             if (!last) read_frags<SLOT>(S + 1, b ^ 1);
             if (S == A_STORE_S) store_a<SLOT ^ 1>();
-            if (S == B_STORE_S) store_b<BSTORE, SLOT ^ 1>();
+            if (S == B_STORE_S) store_b<0, SLOT ^ 1>();
             mfmas(b, 0, nmf);
             __builtin_amdgcn_sched_barrier(0);
             return;
         }
+        constexpr int NT_ = (nmf > NFR ? nmf : NFR);
+        if constexpr (FAST) {
+            const u32x4 rb_ = srsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            const u32x4 ra_ = srsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            const int aslot = ring2(as_cur);           // ring slot of the A slice two ahead
+#pragma unroll
+            for (int t = 0; t < NT_; ++t) {
+                const int gt = S * NMF + t;
+                if (t < nmf) mfma_one(b, t);
+                if (t < NFR) read_frag<SLOT>(S + 1 < SUB ? S + 1 : 0, t, b ^ 1);
+                if (SPREAD) {
+                    const int vi = (gt - VM_FIRST) / VM_STRIDE;  // load number at this slot
+                    if (gt >= VM_FIRST && (gt - VM_FIRST) % VM_STRIDE == 0 && vi < NVM)
+                        issue_dma<SLOT>(vi, aslot, ra_, rb_);
+                } else if (gt == 0) {
+#pragma unroll
+                    for (int vi = 0; vi < NVM; ++vi) issue_dma<SLOT>(vi, aslot, ra_, rb_);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
         const __amdgpu_buffer_rsrc_t rb_rsrc = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
         const __amdgpu_buffer_rsrc_t ra_rsrc = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
-        constexpr int NT_ = (nmf > NFR ? nmf : NFR);
 #pragma unroll
         for (int t = 0; t < NT_; ++t) {
             const int gt = S * NMF + t;
@@ -550,24 +709,24 @@ struct Engine {
             if (SPREAD) {
                 const int vi = (gt - VM_FIRST) / VM_STRIDE;  // load number at this slot
                 if (gt >= VM_FIRST && (gt - VM_FIRST) % VM_STRIDE == 0 && vi < NVM)
-                    issue_load<SLOT>(vi, ra_rsrc, rb_rsrc, BSET);
+                    issue_load<0>(vi, ra_rsrc, rb_rsrc);
             } else if (gt == 0) {
 #pragma unroll
-                for (int vi = 0; vi < NVM; ++vi) issue_load<SLOT>(vi, ra_rsrc, rb_rsrc, BSET);
+                for (int vi = 0; vi < NVM; ++vi) issue_load<0>(vi, ra_rsrc, rb_rsrc);
             }
             const int wi = (gt - ST_FIRST) / VM_STRIDE;  // B write number at this slot
-            if (gt >= ST_FIRST && (gt - ST_FIRST) % VM_STRIDE == 0 && wi < 8) store_b_one<BSTORE, SLOT ^ 1>(wi);
-            if (!A_DMA && S == A_STORE_S && t < CA) {
+            if (gt >= ST_FIRST && (gt - ST_FIRST) % VM_STRIDE == 0 && wi < NBW) store_b_one<0, SLOT ^ 1>(wi);
+            if (S == A_STORE_S && t < CA) {
                 if (Cfg::NA % NT == 0 || t * NT + tid < Cfg::NA)
-                    *reinterpret_cast<u32x4*>(lds + (SLOT ^ 1) * Cfg::A_SLOT + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[0][t];
+                    *reinterpret_cast<u32x4*>(lds + (SLOT ^ 1) * Cfg::A_SLOT + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[t];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         // B writes that did not fit before the barrier slots
         if (last) {
 #pragma unroll
-            for (int wj = 0; wj < 8; ++wj)
-                if (ST_FIRST + wj * VM_STRIDE >= S * NMF + NT_) store_b_one<BSTORE, SLOT ^ 1>(wj);
+            for (int wj = 0; wj < NBW; ++wj)
+                if (ST_FIRST + wj * VM_STRIDE >= S * NMF + NT_) store_b_one<0, SLOT ^ 1>(wj);
         }
     }
 
@@ -576,51 +735,68 @@ struct Engine {
         (substep<SLOT, S>(nx), ...);
     }
 
-    // One K step over LDS slot SLOT (fragments of its sub-step 0 already in buffer
-    // 0).  Slot SLOT^1, which every wave finished reading before the last barrier,
-    // receives the next slice; after this step's barrier its sub-step 0 fragments
-    // are read, behind the last HOLD MFMAs of this step.  Past the last slice these
+    // Fast path barrier: this wave's loads older than its last `pending` VMEM
+    // operations (they return in order) have landed and its LDS accesses are
+    // done; then the workgroup meets.
+    template <int pending>
+    __device__ __forceinline__ void barrier_after_loads() {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(pending) : "memory");
+    }
+
+    // One K step over B slot SLOT (fragments of its sub-step 0 already in buffer
+    // 0).  Slot SLOT^1 (and on the fast path the A ring slot two ahead), which
+    // every wave finished reading before the last barrier, receives a later slice;
+    // after this step's barrier the sub-step 0 fragments of the next slot are
+    // read, behind the last HOLD MFMAs of this step.  Past the last slice these
     // writes and reads carry zeros nobody uses, so every step has the same shape
     // and the accumulators stay in one set of registers through the loop.
     template <int SLOT>
     __device__ __forceinline__ void kstep(const Next& nx) {
         constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
         substeps<SLOT>(nx, std::make_integer_sequence<int, SUB>{});
-        if (A_DMA) {
-            // each wave's direct-to-LDS loads must have landed before the barrier
-            // that hands the slot to the other waves (the B loads of this step,
-            // issued just before them, are waited for with them)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (FAST) {
+            barrier_after_loads<A_DMA_N>();   // the A loads of this step stay in flight
+            advance_a();
+        } else {
+            __syncthreads();
         }
-        __syncthreads();
         read_frags<SLOT ^ 1>(0, 0);
         mfmas(LB, NMF - Cfg::HOLD, NMF);
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Prologue: slice 0 in slot 0 with its first fragments read; the fast path also
-    // starts B slice 1 (register set 1).  `nx` then describes the first step's loads.
-    __device__ __forceinline__ void prologue(int m0, int n0, int k0, int n1, int k1, bool two) {
-        load_b<0>(n0, k0, true);
-        if (A_DMA) {
-            dma_a<0>(m0, k0, true);
-            load_b<B_DIST - 1>(n1, k1, two);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Prologue: slice p0 in slot 0 (A: ring slot as_cur) with its first fragments
+    // read; the fast path also has A slice p1 in flight into the next ring slot.
+    // The first K step then loads the slices after.
+    __device__ __forceinline__ void prologue(const Next& p0, const Next& p1) {
+        if constexpr (FAST) {
+            dma_b(0, p0.n0, p0.kb, true);
+            dma_a(as_cur, p0.m0, p0.ka, true);
+            dma_a(ring1(as_cur), p1.m0, p1.ka, p1.va);
+            barrier_after_loads<A_DMA_N>();
         } else {
-            load_a(m0, k0, true);
+            load_b<0>(p0.n0, p0.kb, true);
+            load_a(p0.m0, p0.ka, true);
             store_a<0>();
+            store_b<0, 0>();
+            __syncthreads();
         }
-        store_b<0, 0>();
-        __syncthreads();
         read_frags<0>(0, 0);
     }
 
-    // Full pipeline for one tile (no epilogue): steps alternate slots 0 and 1; an
+    // End of the program: the direct-to-LDS loads of slices past the last one are
+    // still in flight after the last barrier; let them land before the waves end
+    // and the workgroup's LDS is handed to another.
+    __device__ __forceinline__ void drain() {
+        if (FAST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    // Full pipeline for one tile (no epilogue): steps alternate B slots 0 and 1; an
     // odd step count runs one slot-0 step first and then pairs starting on slot 1.
     __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
-        prologue(m0, n0, 0, n0, 1, ks > 1);
-        auto nx = [&](int k) {  // loads issued by step k
-            return Next{m0, k + 1, k + 1 < ks, n0, k + B_DIST, k + B_DIST < ks};
+        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1});
+        auto nx = [&](int k) {  // loads of step k
+            return Next{m0, k + DA, k + DA < ks, n0, k + 1, k + 1 < ks};
         };
         int k = 0;
         if (ks & 1) {
@@ -675,8 +851,9 @@ struct Engine {
 // (prologue loads, K loop with two slices in flight, epilogue).
 template <class Cfg, class TI, class TO, bool MASKED, int MODE>
 __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-    Engine<Cfg, TI, TO, MASKED> e(g, lds);
+    __shared__ __attribute__((aligned(16))) char lds_a[Cfg::A_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::B_BYTES];
+    Engine<Cfg, TI, TO, MASKED> e(g, lds_a, lds_b);
     const ProgramWork w(g.s, blockIdx.x);
     const int ntiles = (MODE == MODE_TILED) ? 1 : w.ntiles;
     for (int i = 0; i < ntiles; ++i) {
@@ -687,6 +864,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
         if (!MASKED || g.s.ks > 0) e.tile_mainloop(m0, n0, g.s.ks);
         e.store_tile(m0, n0);
     }
+    e.drain();
 }
 
 // Position of the flattened loop: cursor plus the origin of its tile.
@@ -713,27 +891,28 @@ struct FlatPos {
 // in flight while item it is multiplied and, at a tile's last K step, stored.
 template <class Cfg, class TI, class TO, bool MASKED>
 __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_a[Cfg::A_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::B_BYTES];
     typedef Engine<Cfg, TI, TO, MASKED> E;
-    E e(g, lds);
+    E e(g, lds_a, lds_b);
     const ProgramWork w(g.s, blockIdx.x);
     const int total = w.total_items();
     if (total == 0) return;
     FlatPos cp{FlatCursor(w), 0, 0};   // item being multiplied
     cp.template coords<Cfg>(g.s);
-    FlatPos la = cp;                   // next item whose A slice is loaded (one ahead)
-    la.template advance<Cfg>(g.s, w);
-    e.prologue(cp.m0, cp.n0, cp.c.k, la.n0, la.c.k, total > 1);
-    FlatPos lb = la;                   // next item whose B slice is loaded (B_DIST ahead)
-    if (E::B_DIST == 2) lb.template advance<Cfg>(g.s, w);
+    FlatPos lb = cp;                   // next item whose B slice is loaded (one ahead)
+    lb.template advance<Cfg>(g.s, w);
+    e.prologue(typename E::Next{cp.m0, cp.c.k, true, cp.n0, cp.c.k, true},
+               typename E::Next{lb.m0, lb.c.k, total > 1, lb.n0, lb.c.k, total > 1});
+    FlatPos la = lb;                   // next item whose A slice is loaded (DA ahead)
+    if (E::DA == 2) la.template advance<Cfg>(g.s, w);
     // cursors past the program's last item produce coordinates that are never read
 
     int it = 0;
     auto step = [&](auto slot_tag) {
         constexpr int SLOT = decltype(slot_tag)::value;
         if (cp.c.k == 0) e.zero_acc();
-        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + 1 < total, lb.n0, lb.c.k,
-                                                it + E::B_DIST < total});
+        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + E::DA < total, lb.n0, lb.c.k, it + 1 < total});
         la.template advance<Cfg>(g.s, w);
         lb.template advance<Cfg>(g.s, w);
         if (cp.c.last_k(w)) e.store_tile(cp.m0, cp.n0);
@@ -754,6 +933,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
             step(S1{});
         }
     }
+    e.drain();
 }
 
 // Schedule trace: one thread per program, the same functions as above.
