@@ -195,16 +195,22 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //    from global memory into LDS with direct-to-LDS buffer loads, no registers
 //    in between:
 //      A ([m][k], 16-byte chunks swizzled by swz(r) below) into a ring of three
-//        slots, two slices ahead of the slice being multiplied;
+//        slots;
 //      B in the slice's natural [k][n] layout (chunks swizzled by f(k) below)
-//        into two slots, one slice ahead, read back as MFMA operands with LDS
-//        transpose reads.
-//    A step issues B first, then A; it ends with each wave waiting for all but
-//    its A loads of this step, then the workgroup barrier.  The 3 + 2 slots of
-//    256 x 64 slices fill the 160 KiB of LDS exactly.  The loads are issued as
-//    inline assembly: the compiler then neither waits for them before LDS reads
-//    it cannot prove disjoint (the ring slot is chosen at run time) nor counts
-//    them, and the one wait the pipeline needs is explicit.
+//        into two slots, read back as MFMA operands with LDS transpose reads.
+//    MFMA operand fragments are read two sub-steps (of 16 k) ahead into four
+//    register buffers, so the workgroup barrier sits in the middle of a K step:
+//    before it the MFMAs of sub-steps 0-1 run while the fragments of 2-3 are
+//    read; the barrier certifies that every wave is done reading this slice and
+//    that the next one has landed; after it the MFMAs of 2-3 run while the next
+//    slice's first fragments are read and the slots this slice freed receive B
+//    two slices ahead and A three ahead -- a full K step for every load to
+//    land.  A step issues B first, then A, and the barrier waits for all but the
+//    A loads of the step before.  The 3 + 2 slots of 256 x 64 slices fill the
+//    160 KiB of LDS exactly.  The loads are issued as inline assembly: the
+//    compiler then neither waits for them before LDS reads it cannot prove
+//    disjoint (the ring slot is chosen at run time) nor counts them, and the one
+//    wait the pipeline needs is explicit.
 //  register (masked edges, or BK = 32): A and B one slice ahead in registers,
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
@@ -225,7 +231,9 @@ struct Engine {
                                  (BK * RBB) % (1024 * NW) == 0 && (NW * RPD) % 8 == 0;
     static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
     static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
-    static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
+    static constexpr int DA = FAST ? 3 : 1;          // A slices in flight ahead of the multiplied one
+    static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
+    static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
     static constexpr int NJB = FN < 4 ? FN : 4;      // per-lane B transpose-read offsets
     // sub-steps that write the next slice into LDS (register path)
     static constexpr int A_STORE_S = SUB > 2 ? SUB - 2 : SUB - 1;
@@ -254,7 +262,7 @@ struct Engine {
 
     u32x4 ra[FAST ? 1 : CA];                 // A slice in flight (register path)
     u32x4 rb[1][KBH];                        // B slice in flight (register path; KBH rows of 8 columns)
-    u32x4 fa[2][FM], fb[2][FN];
+    u32x4 fa[NFB][FM], fb[NFB][FN];
     f32x16 acc[FM][FN];
 
     __device__ __forceinline__ Engine(const GemmArgs& g_, char* lds_a, char* lds_b) : g(g_), lds(lds_a), ldsb(lds_b) {
@@ -584,13 +592,16 @@ struct Engine {
         for (int j = 0; j < FN; ++j) fb[buf][j] = read_b<SLOT>(s, j);
     }
 
-    // Fragment number idx (A blocks first, then B blocks) of sub-step s.
+    // Fragment number idx of sub-step s, in the order the MFMAs of a sub-step
+    // first need them: A block 0, the B blocks, then A blocks 1, 2, ...
     template <int SLOT>
     __device__ __forceinline__ void read_frag(int s, int idx, int buf) {
-        if (idx < FM)
-            fa[buf][idx] = read_a<SLOT>(s, idx);
+        if (idx == 0)
+            fa[buf][0] = read_a<SLOT>(s, 0);
+        else if (idx <= FN)
+            fb[buf][idx - 1] = read_b<SLOT>(s, idx - 1);
         else
-            fb[buf][idx - FM] = read_b<SLOT>(s, idx - FM);
+            fa[buf][idx - FN] = read_a<SLOT>(s, idx - FN);
     }
 
     // MFMA number t of a sub-step, in (i, j) order.
@@ -610,7 +621,7 @@ struct Engine {
     }
 
     // Slices loaded by a K step: A slice ka of tile row origin m0 (DA slices ahead
-    // of the one multiplied) and B slice kb of tile column origin n0 (one ahead).
+    // of the one multiplied) and B slice kb of tile column origin n0 (DB ahead).
     // A false `v*` means past the last slice: nothing is read and zeros flow.
     struct Next {
         int m0, ka;
@@ -750,30 +761,75 @@ struct Engine {
     // read, behind the last HOLD MFMAs of this step.  Past the last slice these
     // writes and reads carry zeros nobody uses, so every step has the same shape
     // and the accumulators stay in one set of registers through the loop.
+    // Fast path, sub-step S of a K step on B slot SLOT: the MFMAs of sub-step S
+    // (fragment buffer S) with the reads of the fragments of sub-step S + 2 mod 4
+    // (into its buffer) spread over them -- of this slice for S < 2, of the next
+    // one (B slot SLOT^1, the ring slot advanced to) for S >= 2 -- and, for
+    // S >= 2, the loads into the slots this slice freed: B (slice nx.kb) into B
+    // slot SLOT, then A (slice nx.ka) into ring slot `aslot`.
+    static constexpr int F_NFR = FM + FN;                            // fragment reads per sub-step
+    static constexpr int F_DS = 2 * NMF >= 2 * NVM ? 2 : 1;          // MFMA slots between loads
+    static_assert(!FAST || 2 * NMF >= NVM, "loads must fit the two sub-steps after the barrier");
+    template <int SLOT, int S>
+    __device__ __forceinline__ void fast_sub(const u32x4& ra_, const u32x4& rb_, int aslot) {
+        constexpr int RS = (S + 2) & 3;
+        constexpr int RSLOT = S < 2 ? SLOT : (SLOT ^ 1);
+        constexpr int NT_ = NMF > F_NFR ? NMF : F_NFR;
+#pragma unroll
+        for (int t = 0; t < NT_; ++t) {
+            if (t < NMF) mfma_one(S, t);
+            if (t < F_NFR) read_frag<RSLOT>(RS, t, RS);
+            if (S >= 2) {
+                const int gt = (S - 2) * NMF + t;
+                const int vi = gt / F_DS;
+                if (gt % F_DS == 0 && vi < NVM) {
+                    if (vi < B_DMA_N)
+                        dma_b_one(SLOT, vi, rb_);
+                    else
+                        dma_a_one(aslot, vi - B_DMA_N, ra_);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     template <int SLOT>
     __device__ __forceinline__ void kstep(const Next& nx) {
+        if constexpr (FAST) {
+            const u32x4 rb_ = srsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            const u32x4 ra_ = srsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            fast_sub<SLOT, 0>(ra_, rb_, 0);
+            fast_sub<SLOT, 1>(ra_, rb_, 0);
+            barrier_after_loads<A_DMA_N>();   // the A loads of the step before stay in flight
+            advance_a();
+            const int aslot = ring2(as_cur);  // the slot this slice held
+            fast_sub<SLOT, 2>(ra_, rb_, aslot);
+            fast_sub<SLOT, 3>(ra_, rb_, aslot);
+            return;
+        }
         constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
         substeps<SLOT>(nx, std::make_integer_sequence<int, SUB>{});
-        if (FAST) {
-            barrier_after_loads<A_DMA_N>();   // the A loads of this step stay in flight
-            advance_a();
-        } else {
-            __syncthreads();
-        }
+        __syncthreads();
         read_frags<SLOT ^ 1>(0, 0);
         mfmas(LB, NMF - Cfg::HOLD, NMF);
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Prologue: slice p0 in slot 0 (A: ring slot as_cur) with its first fragments
-    // read; the fast path also has A slice p1 in flight into the next ring slot.
-    // The first K step then loads the slices after.
-    __device__ __forceinline__ void prologue(const Next& p0, const Next& p1) {
+    // Prologue: slice p0 in slot 0 (A: ring slot as_cur) with the fragments of
+    // its first sub-step read (fast path: of its first two).  The fast path also
+    // has slices p1 (B and A) and p2 (A) in flight into the next slots.  The first
+    // K step then loads the slices after.
+    __device__ __forceinline__ void prologue(const Next& p0, const Next& p1, const Next& p2) {
         if constexpr (FAST) {
             dma_b(0, p0.n0, p0.kb, true);
             dma_a(as_cur, p0.m0, p0.ka, true);
+            dma_b(1, p1.n0, p1.kb, p1.vb);
             dma_a(ring1(as_cur), p1.m0, p1.ka, p1.va);
-            barrier_after_loads<A_DMA_N>();
+            dma_a(ring2(as_cur), p2.m0, p2.ka, p2.va);
+            barrier_after_loads<B_DMA_N + 2 * A_DMA_N>();
+            read_frags<0>(0, 0);
+            read_frags<0>(1, 1);
+            return;
         } else {
             load_b<0>(p0.n0, p0.kb, true);
             load_a(p0.m0, p0.ka, true);
@@ -794,9 +850,10 @@ struct Engine {
     // Full pipeline for one tile (no epilogue): steps alternate B slots 0 and 1; an
     // odd step count runs one slot-0 step first and then pairs starting on slot 1.
     __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
-        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1});
+        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1},
+                 Next{m0, 2, ks > 2, n0, 2, ks > 2});
         auto nx = [&](int k) {  // loads of step k
-            return Next{m0, k + DA, k + DA < ks, n0, k + 1, k + 1 < ks};
+            return Next{m0, k + DA, k + DA < ks, n0, k + DB, k + DB < ks};
         };
         int k = 0;
         if (ks & 1) {
@@ -900,19 +957,23 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     if (total == 0) return;
     FlatPos cp{FlatCursor(w), 0, 0};   // item being multiplied
     cp.template coords<Cfg>(g.s);
-    FlatPos lb = cp;                   // next item whose B slice is loaded (one ahead)
-    lb.template advance<Cfg>(g.s, w);
+    FlatPos p1 = cp;                   // items 1 and 2
+    p1.template advance<Cfg>(g.s, w);
+    FlatPos p2 = p1;
+    p2.template advance<Cfg>(g.s, w);
     e.prologue(typename E::Next{cp.m0, cp.c.k, true, cp.n0, cp.c.k, true},
-               typename E::Next{lb.m0, lb.c.k, total > 1, lb.n0, lb.c.k, total > 1});
-    FlatPos la = lb;                   // next item whose A slice is loaded (DA ahead)
-    if (E::DA == 2) la.template advance<Cfg>(g.s, w);
+               typename E::Next{p1.m0, p1.c.k, total > 1, p1.n0, p1.c.k, total > 1},
+               typename E::Next{p2.m0, p2.c.k, total > 2, p2.n0, p2.c.k, total > 2});
+    FlatPos lb = E::DB == 2 ? p2 : p1; // next item whose B slice is loaded (DB ahead)
+    FlatPos la = E::DA == 1 ? p1 : p2; // next item whose A slice is loaded (DA ahead)
+    if (E::DA == 3) la.template advance<Cfg>(g.s, w);
     // cursors past the program's last item produce coordinates that are never read
 
     int it = 0;
     auto step = [&](auto slot_tag) {
         constexpr int SLOT = decltype(slot_tag)::value;
         if (cp.c.k == 0) e.zero_acc();
-        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + E::DA < total, lb.n0, lb.c.k, it + 1 < total});
+        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + E::DA < total, lb.n0, lb.c.k, it + E::DB < total});
         la.template advance<Cfg>(g.s, w);
         lb.template advance<Cfg>(g.s, w);
         if (cp.c.last_k(w)) e.store_tile(cp.m0, cp.n0);
