@@ -9,7 +9,11 @@ dense fp16 MFMA peak, from HIP events on the launch stream), the HBM traffic the
 last hardware-counter profile measured for this kernel source, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME] [--sweep]
+    python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME] [--sweep] [--ksweep]
+
+--sweep times every order x remap x mode at the workload; --ksweep times the
+grouped persistent loop against the flattened cross-tile loop over the K sweep
+at 16384 x 16384 (tables on stderr, before the JSON line).
 
 Schedules are written order[+remap]/mode[/P<programs>][/tile], e.g.
 "grouped8+remap/tiled", "rowmajor/persistent/P256", "grouped8/crosstile".
@@ -130,7 +134,8 @@ def cpu_baseline(A, B, w, budget_s: float):
 
 PMC_SCHEDULES = {
     "gemm_16384x16384x4096_f16": [f"{o}{r}/{m}" for o in ("rowmajor", "grouped4", "grouped8", "grouped16")
-                                  for r in ("", "+remap") for m in ("tiled", "persistent")],
+                                  for r in ("", "+remap") for m in ("tiled", "persistent")]
+                                 + ["rowmajor/crosstile", "grouped8+remap/crosstile"],
     "gemm_8192x8192x4096_f16": [f"{o}{r}/{m}" for o in ("rowmajor", "grouped8")
                                 for r in ("", "+remap") for m in ("tiled", "persistent")],
 }
@@ -168,6 +173,26 @@ def pmc_target(ts, torch, np, workloads):
         del a, b, c
 
 
+KSWEEP_SCHEDULES = ("grouped8+remap/persistent", "grouped8+remap/crosstile")
+
+
+def ksweep(ts, torch, np, workloads, steps):
+    """Grouped persistent vs persistent + cross-tile over the K sweep (stderr table)."""
+    for w in workloads.K_SWEEP:
+        A, B = workloads.inputs(w)
+        a = torch.from_numpy(A.view(np.int16)).view(torch.float16).cuda()
+        b = torch.from_numpy(B.view(np.int16)).view(torch.float16).cuda()
+        c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        flops = 2.0 * w.M * w.N * w.K
+        hbm = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N)   # compulsory bytes, fp16
+        for lab in KSWEEP_SCHEDULES:
+            r = time_gemm(ts, torch, a, b, c, parse_schedule(lab), steps, 3)
+            t = r["median_ms"] * 1e-3
+            log(f"ksweep K={w.K:5d} {lab:28s} median {r['median_ms']:.4f} ms  {flops / t / 1e12:8.1f} TFLOP/s  "
+                f"compulsory {hbm / t / 1e9:7.1f} GB/s")
+        del a, b, c
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +201,8 @@ def main():
     ap.add_argument("--workload", default="gemm_16384x16384x4096_f16")
     ap.add_argument("--schedule", default=DEFAULT_SCHEDULE)
     ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
+    ap.add_argument("--ksweep", action="store_true",
+                    help="also time persistent vs cross-tile over the K sweep (table on stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-target", action="store_true",
@@ -207,6 +234,8 @@ def main():
     c = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
     flops = 2.0 * w.M * w.N * w.K
 
+    if args.ksweep:
+        ksweep(ts, torch, np, workloads, max(10, args.steps))
     if args.sweep:
         labels = []
         for order in ("rowmajor", "grouped4", "grouped8", "grouped16"):
