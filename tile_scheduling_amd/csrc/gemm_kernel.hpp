@@ -86,11 +86,12 @@ struct TileCfg {
     static constexpr int CB = (NB + NT - 1) / NT;       // B blocks per thread
     static constexpr int ROW_BYTES = BK * 2;            // one LDS row (m or n) of a slice
     static constexpr int A_SLOT = BM * ROW_BYTES, B_SLOT = BN * ROW_BYTES;
-    // LDS: A slots [A0][A1]([A2]) and B slots [B0][B1] (two arrays); BK = 64 tiles
-    // get a third A slot when it fits
-    static constexpr int A_RING = (BK == 64 && 3 * A_SLOT + 2 * B_SLOT <= 160 * 1024) ? 3 : 2;
-    static constexpr int A_BYTES = A_RING * A_SLOT, B_BYTES = 2 * B_SLOT;
-    static constexpr int LDS_BYTES = A_BYTES + B_BYTES;
+    // LDS: A slots A0, A1, B slots B0, B1 and (BK = 64 tiles) a 4 KiB epilogue
+    // staging area per wave, each its own array
+    static constexpr int A_BYTES = 2 * A_SLOT, B_BYTES = 2 * B_SLOT;
+    static constexpr int STAGE_W = 4096;
+    static constexpr int C_BYTES = BK == 64 ? (NT / 64) * STAGE_W : 0;
+    static constexpr int LDS_BYTES = A_BYTES + B_BYTES + C_BYTES;
     static constexpr int HOLD = (FM * FN >= 16) ? 8 : FM * FN / 2;  // MFMAs issued after the barrier
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tile must be whole 32x32 blocks");
     static_assert(BK % 16 == 0 && KCH <= 8 && (KCH & (KCH - 1)) == 0, "BK must be 16, 32 or 64");
@@ -194,8 +195,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //  fast (unmasked, BK = 64, 128- or 256-wide tiles).  Both operands go straight
 //    from global memory into LDS with direct-to-LDS buffer loads, no registers
 //    in between:
-//      A ([m][k], 16-byte chunks swizzled by swz(r) below) into a ring of three
-//        slots;
+//      A ([m][k], 16-byte chunks swizzled by swz(r) below) into two slots;
 //      B in the slice's natural [k][n] layout (chunks swizzled by f(k) below)
 //        into two slots, read back as MFMA operands with LDS transpose reads.
 //    MFMA operand fragments are read two sub-steps (of 16 k) ahead into four
@@ -203,14 +203,19 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //    before it the MFMAs of sub-steps 0-1 run while the fragments of 2-3 are
 //    read; the barrier certifies that every wave is done reading this slice and
 //    that the next one has landed; after it the MFMAs of 2-3 run while the next
-//    slice's first fragments are read and the slots this slice freed receive B
-//    two slices ahead and A three ahead -- a full K step for every load to
-//    land.  A step issues B first, then A, and the barrier waits for all but the
-//    A loads of the step before.  The 3 + 2 slots of 256 x 64 slices fill the
-//    160 KiB of LDS exactly.  The loads are issued as inline assembly: the
-//    compiler then neither waits for them before LDS reads it cannot prove
-//    disjoint (the ring slot is chosen at run time) nor counts them, and the one
-//    wait the pipeline needs is explicit.
+//    slice's first fragments are read and the slots this slice freed receive the
+//    slices two ahead -- a full K step for every load to land.  The barrier
+//    waits for every load of the step before (and nothing issued later).  Each
+//    slot is its own LDS array and every slot index is a compile-time constant,
+//    so the compiler can tell that a load into one slot never touches the slot
+//    being read, and in the tiled and persistent loops the waits it places for
+//    its own bookkeeping are already met by the explicit one (in the flattened
+//    loop it still places a few full waits).  The cross-wave wait the pipeline
+//    needs is explicit before the barrier.
+//    The epilogue stages each wave's tile through a private 4 KiB of LDS, so that
+//    every global store writes whole 128- or 256-byte row segments.  2 x 32 KiB
+//    of A, 2 x 32 KiB of B and 8 x 4 KiB of staging fill the 160 KiB of LDS of
+//    the 256 x 256 x 64 tile.
 //  register (masked edges, or BK = 32): A and B one slice ahead in registers,
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
@@ -226,12 +231,12 @@ struct Engine {
     static constexpr int NBN = BN / 8;               // B loader blocks along n
     static constexpr int RBB = BN * 2;               // bytes of one [k][n] B row (fast path)
     static constexpr int LPR = RBB / 16, RPD = 64 / LPR;   // B load lanes per row, rows per 1 KiB load
-    static constexpr bool FAST = !MASKED && RB == 128 && Cfg::A_RING == 3 && (BM * RB) % (1024 * NW) == 0 &&
+    static constexpr bool FAST = !MASKED && RB == 128 && Cfg::C_BYTES > 0 && (BM * RB) % (1024 * NW) == 0 &&
                                  LPR >= 16 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
                                  (BK * RBB) % (1024 * NW) == 0 && (NW * RPD) % 8 == 0;
     static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
     static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
-    static constexpr int DA = FAST ? 3 : 1;          // A slices in flight ahead of the multiplied one
+    static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
     static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
     static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
     static constexpr int NJB = FN < 4 ? FN : 4;      // per-lane B transpose-read offsets
@@ -241,18 +246,16 @@ struct Engine {
     static_assert(CB == 1, "one B loader block per thread");
 
     const GemmArgs& g;
-    char* lds;            // A slots
-    char* ldsb;           // B slots
+    char* la[2];          // A slots
+    char* lb[2];          // B slots
+    char* ldsc;           // epilogue staging (fast path)
     int tid, lane, wm, wn, wave;
-    int as_cur;           // fast path: A ring slot of the slice being multiplied
 
     // per-lane LDS byte offsets
-    uint32_t a_rd[SUB];   // A fragment read of block 0 at sub-step s (block i: + i*32*RB);
-                          // fast path: includes the current ring slot
+    uint32_t a_rd[SUB];   // A fragment read of block 0 at sub-step s (block i: + i*32*RB)
     uint32_t b_rd[SUB];   // register path: B fragment read, as a_rd
     uint32_t bt_rd[NJB];  // fast path: B transpose read of block u (block j: bt_rd[j % 4] + (j / 4) * 256)
     uint32_t b_dg[2];     // fast path: B load global offset, by bit 3 of its first row
-    uint32_t lds_a_at, lds_b_at;  // LDS addresses of the A and B slots
     uint32_t a_wr[2];     // register path: A chunk c at a_wr[c&1] + c*A_ROWS_PER_C*RB
     uint32_t b_wr[8];     // B write j of the loader block (see b_wr_at)
     uint32_t b_sel[2];    // register path: byte-permute selector of B writes with even / odd j
@@ -265,15 +268,13 @@ struct Engine {
     u32x4 fa[NFB][FM], fb[NFB][FN];
     f32x16 acc[FM][FN];
 
-    __device__ __forceinline__ Engine(const GemmArgs& g_, char* lds_a, char* lds_b) : g(g_), lds(lds_a), ldsb(lds_b) {
+    __device__ __forceinline__ Engine(const GemmArgs& g_, char* a0, char* a1, char* b0, char* b1, char* lds_c)
+        : g(g_), la{a0, a1}, lb{b0, b1}, ldsc(lds_c) {
         tid = threadIdx.x;
         lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         wm = wave / Cfg::WN;
         wn = wave % Cfg::WN;
-        as_cur = 0;
-        lds_a_at = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_a;
-        lds_b_at = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_b;
         const int r32 = lane & 31, hk = lane >> 5;
         // Rows of [m][k] (and, on the register path, [n][k]) slices are swizzled by
         // swz(r) = (r ^ (r >> 3)) mod KCH.  A fragment row is (32-aligned base) +
@@ -412,58 +413,35 @@ struct Engine {
                                                  __builtin_amdgcn_readfirstlane(valid ? -1 : 0), kBufferFlags);
     }
 
-    // Fast path: ring slot after / two after slot `s`.
-    static __device__ __forceinline__ int ring1(int s) { return s == 2 ? 0 : s + 1; }
-    static __device__ __forceinline__ int ring2(int s) { return s == 0 ? 2 : s - 1; }
-
-    // Fast path: buffer resource as four scalar registers, for inline assembly.
-    __device__ __forceinline__ u32x4 srsrc(const uint16_t* p, bool valid) const {
-        const uint64_t a = (uint64_t)(uintptr_t)p;
-        u32x4 r;
-        r[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-        r[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
-        r[2] = (uint32_t)__builtin_amdgcn_readfirstlane(valid ? -1 : 0);
-        r[3] = (uint32_t)kBufferFlags;
-        return r;
-    }
-
     // Fast path: one direct-to-LDS load of 16 bytes per lane; lane l's bytes land at
-    // LDS address m0 + 16 l.  The M0 write needs one wait state before the load.
-    static __device__ __forceinline__ void dma16(const u32x4& r, uint32_t voff, int soff, uint32_t m0) {
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     ::"s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+    // dst + 16 l.
+    static __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, uint32_t voff, int soff, char* dst) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff, soff, 0, 0);
     }
 
-    // Fast path: 1 KiB A load number c of this wave, into ring slot `slot`.
-    __device__ __forceinline__ void dma_a_one(int slot, int c, const u32x4& r) {
+    // Fast path: 1 KiB A load number c of this wave, into A slot `slot`.
+    template <int SLOT>
+    __device__ __forceinline__ void dma_a_one(int c, const __amdgpu_buffer_rsrc_t& r) {
         const int grp = c * NW + wave;                     // 8-row group (1 KiB)
-        dma16(r, a_go[((c * NW) >> 2) & 1], (int)((long long)grp * 8 * g.lda * 2),
-              lds_a_at + (uint32_t)(slot * Cfg::A_SLOT + grp * 1024));
+        dma16(r, a_go[((c * NW) >> 2) & 1], (int)((long long)grp * 8 * g.lda * 2), la[SLOT] + grp * 1024);
     }
-    __device__ __forceinline__ void dma_a(int slot, int m0, int k, bool valid) {
-        const u32x4 r = srsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
+    template <int SLOT>
+    __device__ __forceinline__ void dma_a(int m0, int k, bool valid) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
 #pragma unroll
-        for (int c = 0; c < A_DMA_N; ++c) dma_a_one(slot, c, r);
+        for (int c = 0; c < A_DMA_N; ++c) dma_a_one<SLOT>(c, r);
     }
     // Fast path: 1 KiB B load number c of this wave, into B slot `slot`.
-    __device__ __forceinline__ void dma_b_one(int slot, int c, const u32x4& r) {
+    template <int SLOT>
+    __device__ __forceinline__ void dma_b_one(int c, const __amdgpu_buffer_rsrc_t& r) {
         const int grp = c * NW + wave;                     // RPD-row group (1 KiB)
-        dma16(r, b_dg[((c * NW * RPD) >> 3) & 1], (int)((long long)grp * RPD * g.ldb * 2),
-              lds_b_at + (uint32_t)(slot * Cfg::B_SLOT + grp * 1024));
+        dma16(r, b_dg[((c * NW * RPD) >> 3) & 1], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
     }
-    __device__ __forceinline__ void dma_b(int slot, int n0, int k, bool valid) {
-        const u32x4 r = srsrc(g.B + (long long)k * BK * g.ldb + n0, valid);
+    template <int SLOT>
+    __device__ __forceinline__ void dma_b(int n0, int k, bool valid) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k * BK * g.ldb + n0, valid);
 #pragma unroll
-        for (int c = 0; c < B_DMA_N; ++c) dma_b_one(slot, c, r);
-    }
-
-    // Fast path: next ring slot; the A read offsets follow it.
-    __device__ __forceinline__ void advance_a() {
-        const bool wrap = as_cur == 2;
-        as_cur = wrap ? 0 : as_cur + 1;
-        const uint32_t d = wrap ? (uint32_t)(-2 * Cfg::A_SLOT) : (uint32_t)Cfg::A_SLOT;
-#pragma unroll
-        for (int s = 0; s < SUB; ++s) a_rd[s] += d;
+        for (int c = 0; c < B_DMA_N; ++c) dma_b_one<SLOT>(c, r);
     }
 
     // A slice k of tile row m0 into registers (register path).
@@ -521,7 +499,7 @@ struct Engine {
     // Register A slice -> LDS slot SLOT (register path).
     template <int SLOT>
     __device__ __forceinline__ void store_a() {
-        char* sa = lds + SLOT * Cfg::A_SLOT;
+        char* sa = la[SLOT];
 #pragma unroll
         for (int c = 0; c < CA; ++c) {
             if (Cfg::NA % NT == 0 || c * NT + tid < Cfg::NA)
@@ -542,7 +520,7 @@ struct Engine {
     template <int SET, int SLOT>
     __device__ __forceinline__ void store_b_one(int j) {
         if (!(Cfg::NB % NT == 0) && !b_active) return;
-        char* sb = ldsb + SLOT * Cfg::B_SLOT;
+        char* sb = lb[SLOT];
         const int d = j >> 1;
         const uint32_t sel = b_sel[j & 1];
         if (KBH == 8) {
@@ -564,11 +542,10 @@ struct Engine {
         for (int j = 0; j < NBW; ++j) store_b_one<SET, SLOT>(j);
     }
 
-    // A fragment of 32-row block i at sub-step s (A slot SLOT on the register path,
-    // the current ring slot on the fast path).
+    // A fragment of 32-row block i at sub-step s from slot SLOT.
     template <int SLOT>
     __device__ __forceinline__ u32x4 read_a(int s, int i) const {
-        const char* base = lds + (FAST ? 0 : SLOT * Cfg::A_SLOT);
+        const char* base = la[SLOT];
         return lds_read16(base, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
     }
 
@@ -576,12 +553,12 @@ struct Engine {
     template <int SLOT>
     __device__ __forceinline__ u32x4 read_b(int s, int j) const {
         if (FAST) {   // two transpose reads: k offsets 0-3 and 4-7 of the lane's half
-            const char* base = ldsb + SLOT * Cfg::B_SLOT + (j >> 2) * 256 + 16 * s * RBB;
+            const char* base = lb[SLOT] + (j >> 2) * 256 + 16 * s * RBB;
             const u32x2 lo = lds_read_tr(base, bt_rd[j & 3]);
             const u32x2 hi = lds_read_tr(base + 4 * RBB, bt_rd[j & 3]);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        return lds_read16(ldsb + SLOT * Cfg::B_SLOT, b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
+        return lds_read16(lb[SLOT], b_rd[(KCH == 8 && (j & 1)) ? (s ^ 2) : s] + j * 32 * RB);
     }
 
     template <int SLOT>
@@ -647,15 +624,6 @@ struct Engine {
     static constexpr int ST_FIRST = SPREAD ? VM_FIRST + NVM * VM_STRIDE : 1 << 20;  // B writes at ST_FIRST + j*VM_STRIDE
     static_assert(NVM < 64, "vmcnt range");
 
-    // Fast path: load number vi of a step on B slot SLOT.
-    template <int SLOT>
-    __device__ __forceinline__ void issue_dma(int vi, int aslot, const u32x4& ra_, const u32x4& rb_) {
-        if (vi < B_DMA_N)
-            dma_b_one(SLOT ^ 1, vi, rb_);
-        else
-            dma_a_one(aslot, vi - B_DMA_N, ra_);
-    }
-
     // Register path (unmasked): load number vi of a step.
     template <int BSET>
     __device__ __forceinline__ void issue_load(int vi, const __amdgpu_buffer_rsrc_t& ra_rsrc,
@@ -689,27 +657,6 @@ struct Engine {
             return;
         }
         constexpr int NT_ = (nmf > NFR ? nmf : NFR);
-        if constexpr (FAST) {
-            const u32x4 rb_ = srsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
-            const u32x4 ra_ = srsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
-            const int aslot = ring2(as_cur);           // ring slot of the A slice two ahead
-#pragma unroll
-            for (int t = 0; t < NT_; ++t) {
-                const int gt = S * NMF + t;
-                if (t < nmf) mfma_one(b, t);
-                if (t < NFR) read_frag<SLOT>(S + 1 < SUB ? S + 1 : 0, t, b ^ 1);
-                if (SPREAD) {
-                    const int vi = (gt - VM_FIRST) / VM_STRIDE;  // load number at this slot
-                    if (gt >= VM_FIRST && (gt - VM_FIRST) % VM_STRIDE == 0 && vi < NVM)
-                        issue_dma<SLOT>(vi, aslot, ra_, rb_);
-                } else if (gt == 0) {
-#pragma unroll
-                    for (int vi = 0; vi < NVM; ++vi) issue_dma<SLOT>(vi, aslot, ra_, rb_);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            return;
-        }
         const __amdgpu_buffer_rsrc_t rb_rsrc = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
         const __amdgpu_buffer_rsrc_t ra_rsrc = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
 #pragma unroll
@@ -729,7 +676,7 @@ struct Engine {
             if (gt >= ST_FIRST && (gt - ST_FIRST) % VM_STRIDE == 0 && wi < NBW) store_b_one<0, SLOT ^ 1>(wi);
             if (S == A_STORE_S && t < CA) {
                 if (Cfg::NA % NT == 0 || t * NT + tid < Cfg::NA)
-                    *reinterpret_cast<u32x4*>(lds + (SLOT ^ 1) * Cfg::A_SLOT + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[t];
+                    *reinterpret_cast<u32x4*>(la[SLOT ^ 1] + a_wr[t & 1] + t * A_ROWS_PER_C * RB) = ra[t];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -764,14 +711,13 @@ struct Engine {
     // Fast path, sub-step S of a K step on B slot SLOT: the MFMAs of sub-step S
     // (fragment buffer S) with the reads of the fragments of sub-step S + 2 mod 4
     // (into its buffer) spread over them -- of this slice for S < 2, of the next
-    // one (B slot SLOT^1, the ring slot advanced to) for S >= 2 -- and, for
-    // S >= 2, the loads into the slots this slice freed: B (slice nx.kb) into B
-    // slot SLOT, then A (slice nx.ka) into ring slot `aslot`.
+    // one (slot SLOT^1) for S >= 2 -- and, for S >= 2, the loads into the slots
+    // this slice freed: B (slice nx.kb), then A (slice nx.ka), into slot SLOT.
     static constexpr int F_NFR = FM + FN;                            // fragment reads per sub-step
     static constexpr int F_DS = 2 * NMF >= 2 * NVM ? 2 : 1;          // MFMA slots between loads
     static_assert(!FAST || 2 * NMF >= NVM, "loads must fit the two sub-steps after the barrier");
     template <int SLOT, int S>
-    __device__ __forceinline__ void fast_sub(const u32x4& ra_, const u32x4& rb_, int aslot) {
+    __device__ __forceinline__ void fast_sub(const __amdgpu_buffer_rsrc_t& ra_, const __amdgpu_buffer_rsrc_t& rb_) {
         constexpr int RS = (S + 2) & 3;
         constexpr int RSLOT = S < 2 ? SLOT : (SLOT ^ 1);
         constexpr int NT_ = NMF > F_NFR ? NMF : F_NFR;
@@ -784,27 +730,30 @@ struct Engine {
                 const int vi = gt / F_DS;
                 if (gt % F_DS == 0 && vi < NVM) {
                     if (vi < B_DMA_N)
-                        dma_b_one(SLOT, vi, rb_);
+                        dma_b_one<SLOT>(vi, rb_);
                     else
-                        dma_a_one(aslot, vi - B_DMA_N, ra_);
+                        dma_a_one<SLOT>(vi - B_DMA_N, ra_);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
+    // `after_store`: the epilogue stores of the tile before were issued after the
+    // loads this barrier waits for; they may stay in flight.
     template <int SLOT>
-    __device__ __forceinline__ void kstep(const Next& nx) {
+    __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false) {
         if constexpr (FAST) {
-            const u32x4 rb_ = srsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
-            const u32x4 ra_ = srsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
-            fast_sub<SLOT, 0>(ra_, rb_, 0);
-            fast_sub<SLOT, 1>(ra_, rb_, 0);
-            barrier_after_loads<A_DMA_N>();   // the A loads of the step before stay in flight
-            advance_a();
-            const int aslot = ring2(as_cur);  // the slot this slice held
-            fast_sub<SLOT, 2>(ra_, rb_, aslot);
-            fast_sub<SLOT, 3>(ra_, rb_, aslot);
+            const __amdgpu_buffer_rsrc_t rb_ = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            const __amdgpu_buffer_rsrc_t ra_ = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            fast_sub<SLOT, 0>(ra_, rb_);
+            fast_sub<SLOT, 1>(ra_, rb_);
+            if (after_store)
+                barrier_after_loads<(NST < 63 ? NST : 63)>();
+            else
+                barrier_after_loads<0>();
+            fast_sub<SLOT, 2>(ra_, rb_);
+            fast_sub<SLOT, 3>(ra_, rb_);
             return;
         }
         constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
@@ -815,18 +764,16 @@ struct Engine {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Prologue: slice p0 in slot 0 (A: ring slot as_cur) with the fragments of
-    // its first sub-step read (fast path: of its first two).  The fast path also
-    // has slices p1 (B and A) and p2 (A) in flight into the next slots.  The first
-    // K step then loads the slices after.
-    __device__ __forceinline__ void prologue(const Next& p0, const Next& p1, const Next& p2) {
+    // Prologue: slice p0 in slot 0 with the fragments of its first sub-step read
+    // (fast path: of its first two); the fast path also has slice p1 in flight
+    // into slot 1.  The first K step then loads the slices after.
+    __device__ __forceinline__ void prologue(const Next& p0, const Next& p1) {
         if constexpr (FAST) {
-            dma_b(0, p0.n0, p0.kb, true);
-            dma_a(as_cur, p0.m0, p0.ka, true);
-            dma_b(1, p1.n0, p1.kb, p1.vb);
-            dma_a(ring1(as_cur), p1.m0, p1.ka, p1.va);
-            dma_a(ring2(as_cur), p2.m0, p2.ka, p2.va);
-            barrier_after_loads<B_DMA_N + 2 * A_DMA_N>();
+            dma_b<0>(p0.n0, p0.kb, true);
+            dma_a<0>(p0.m0, p0.ka, true);
+            dma_b<1>(p1.n0, p1.kb, p1.vb);
+            dma_a<1>(p1.m0, p1.ka, p1.va);
+            barrier_after_loads<B_DMA_N + A_DMA_N>();
             read_frags<0>(0, 0);
             read_frags<0>(1, 1);
             return;
@@ -850,8 +797,7 @@ struct Engine {
     // Full pipeline for one tile (no epilogue): steps alternate B slots 0 and 1; an
     // odd step count runs one slot-0 step first and then pairs starting on slot 1.
     __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
-        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1},
-                 Next{m0, 2, ks > 2, n0, 2, ks > 2});
+        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1});
         auto nx = [&](int k) {  // loads of step k
             return Next{m0, k + DA, k + DA < ks, n0, k + DB, k + DB < ks};
         };
@@ -870,8 +816,66 @@ struct Engine {
         }
     }
 
+    // Fast-path epilogue: each wave converts RS rows of its sub-tile at a time into
+    // its own 4 KiB of LDS ([row][TN] of the output type, 16-byte chunks XOR-
+    // swizzled by row so that the column writes and the row reads are free of bank
+    // conflicts) and writes them back to C as whole row segments: lane l of a
+    // 16-byte store covers chunk l mod CPR of row l / CPR, so a store instruction
+    // writes 1 KiB of complete rows.  Lanes of a 32-row block whose row is not in
+    // the current group skip the LDS write.
+    typedef typename Out<TO>::T OutT;
+    static constexpr int OSZ = sizeof(OutT);
+    static constexpr int ROWB = Cfg::TN * OSZ;                  // bytes of one sub-tile row
+    static constexpr int CPR = ROWB / 16;                       // 16-byte chunks per row
+    static constexpr int RS = Cfg::STAGE_W / ROWB;              // rows per staging round
+    static constexpr int NST = FAST ? FM * (32 / RS) * (Cfg::STAGE_W / 1024) : 0;  // stores per tile
+    static_assert(!FAST || (RS >= 1 && 32 % RS == 0 && (CPR == 8 || CPR == 16 || CPR == 32 || CPR == 64)),
+                  "staging shape");
+    static __device__ __forceinline__ int stage_swz(int r) { return (CPR == 8 ? (r >> 1) : r) & (CPR - 1); }
+
+    __device__ __forceinline__ void store_tile_staged(int m0, int n0) {
+        const int r32 = lane & 31, hk = lane >> 5;
+        char* st = ldsc + wave * Cfg::STAGE_W;
+        OutT* C = reinterpret_cast<OutT*>(g.C);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int h = 0; h < 32 / RS; ++h) {
+                const int r = r32 - h * RS;   // row within this round
+                if (r >= 0 && r < RS) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            // columns 32 j + 8 q + 4 hk .. + 3 of row r
+                            const int byte = (32 * j + 8 * q + 4 * hk) * OSZ;
+                            const int ch = (byte >> 4) ^ stage_swz(r);
+                            char* dst = st + r * ROWB + ch * 16 + (byte & 15);
+                            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                          acc[i][j][4 * q + 3]};
+                            Out<TO>::store4(reinterpret_cast<OutT*>(dst), v, 4, true);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < Cfg::STAGE_W / 1024; ++u) {
+                    const int off = u * 1024 + lane * 16;
+                    const int row = off / ROWB, ch = (off % ROWB) >> 4;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * ROWB + ((ch ^ stage_swz(row)) << 4));
+                    const long long m = m0 + wm * Cfg::TM + i * 32 + h * RS + row;
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(C + m * g.ldc + n0 + wn * Cfg::TN) + ch * 16) = v;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
     // Accumulators -> C (round to the output type), masked to M x N.
     __device__ __forceinline__ void store_tile(int m0, int n0) {
+        if constexpr (FAST) {
+            store_tile_staged(m0, n0);
+            return;
+        }
         typedef typename Out<TO>::T T;
         T* C = reinterpret_cast<T*>(g.C);
         const int r32 = lane & 31, hk = lane >> 5;
@@ -908,9 +912,10 @@ struct Engine {
 // (prologue loads, K loop with two slices in flight, epilogue).
 template <class Cfg, class TI, class TO, bool MASKED, int MODE>
 __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char lds_a[Cfg::A_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::B_BYTES];
-    Engine<Cfg, TI, TO, MASKED> e(g, lds_a, lds_b);
+    __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
+    Engine<Cfg, TI, TO, MASKED> e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
     const ProgramWork w(g.s, blockIdx.x);
     const int ntiles = (MODE == MODE_TILED) ? 1 : w.ntiles;
     for (int i = 0; i < ntiles; ++i) {
@@ -948,35 +953,35 @@ struct FlatPos {
 // in flight while item it is multiplied and, at a tile's last K step, stored.
 template <class Cfg, class TI, class TO, bool MASKED>
 __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) char lds_a[Cfg::A_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds_b[Cfg::B_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
     typedef Engine<Cfg, TI, TO, MASKED> E;
-    E e(g, lds_a, lds_b);
+    E e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
     const ProgramWork w(g.s, blockIdx.x);
     const int total = w.total_items();
     if (total == 0) return;
     FlatPos cp{FlatCursor(w), 0, 0};   // item being multiplied
     cp.template coords<Cfg>(g.s);
-    FlatPos p1 = cp;                   // items 1 and 2
+    FlatPos p1 = cp;                   // item 1
     p1.template advance<Cfg>(g.s, w);
-    FlatPos p2 = p1;
-    p2.template advance<Cfg>(g.s, w);
     e.prologue(typename E::Next{cp.m0, cp.c.k, true, cp.n0, cp.c.k, true},
-               typename E::Next{p1.m0, p1.c.k, total > 1, p1.n0, p1.c.k, total > 1},
-               typename E::Next{p2.m0, p2.c.k, total > 2, p2.n0, p2.c.k, total > 2});
-    FlatPos lb = E::DB == 2 ? p2 : p1; // next item whose B slice is loaded (DB ahead)
-    FlatPos la = E::DA == 1 ? p1 : p2; // next item whose A slice is loaded (DA ahead)
-    if (E::DA == 3) la.template advance<Cfg>(g.s, w);
+               typename E::Next{p1.m0, p1.c.k, total > 1, p1.n0, p1.c.k, total > 1});
+    FlatPos ld = p1;                   // next item whose slices are loaded (DA = DB ahead)
+    static_assert(E::DA == E::DB, "one load cursor");
+    if (E::DA == 2) ld.template advance<Cfg>(g.s, w);
     // cursors past the program's last item produce coordinates that are never read
 
     int it = 0;
+    bool stored = false;               // the item before ended a tile (its stores are in flight)
     auto step = [&](auto slot_tag) {
         constexpr int SLOT = decltype(slot_tag)::value;
         if (cp.c.k == 0) e.zero_acc();
-        e.template kstep<SLOT>(typename E::Next{la.m0, la.c.k, it + E::DA < total, lb.n0, lb.c.k, it + E::DB < total});
-        la.template advance<Cfg>(g.s, w);
-        lb.template advance<Cfg>(g.s, w);
-        if (cp.c.last_k(w)) e.store_tile(cp.m0, cp.n0);
+        e.template kstep<SLOT>(typename E::Next{ld.m0, ld.c.k, it + E::DA < total, ld.n0, ld.c.k, it + E::DA < total},
+                               stored);
+        ld.template advance<Cfg>(g.s, w);
+        stored = cp.c.last_k(w);
+        if (stored) e.store_tile(cp.m0, cp.n0);
         cp.template advance<Cfg>(g.s, w);
         ++it;
     };
