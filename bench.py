@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+MFMA_TFLOPS_PER_GHZ = 256 * 4 * 1024 / 1000.0   # 256 CUs x 4 SIMDs x 1024 FLOP/clk, per GHz
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 METRIC = "fp16 GEMM TFLOPS (2MNK/s) + % MFMA peak at M=N=16384, K=4096"
 DEFAULT_SCHEDULE = "grouped8+remap/persistent"
@@ -259,6 +260,20 @@ def main():
     log(f"timed {args.steps} steps: wall {ms_per_step:.4f} ms/step, events {r['event_ms']:.4f} ms/launch "
         f"(median {r['median_ms']:.4f}, min {r['min_ms']:.4f}, max {r['max_ms']:.4f})")
 
+    # One more launch with the per-workgroup clock record, outside the timed region:
+    # the shader clock the board's power limit allowed, and the MFMA peak at it.
+    clk = ts.clock_ghz(ts.gemm_clocked(a, b, c, schedule=sched))
+    torch.cuda.synchronize()
+    peak_at_clock = MFMA_TFLOPS_PER_GHZ * clk["mean"]
+    clock = {"ghz": round(clk["mean"], 4), "ghz_min": round(clk["min"], 4), "ghz_max": round(clk["max"], 4),
+             "mfma_peak_at_clock": round(peak_at_clock, 1), "frac_at_clock": round(achieved / peak_at_clock, 4),
+             "source": "s_memtime over s_memrealtime (100 MHz) per workgroup, one launch after the timed ones; "
+                       "loop peak: no-memory MFMA probe, 8 waves per CU"}
+    loop_peak = ts.mfma_loop_tflops()
+    clock["mfma_loop_peak"] = round(loop_peak, 1)
+    clock["frac_of_loop_peak"] = round(achieved / loop_peak, 4)
+    log(f"clock {clock}")
+
     traffic = measured_traffic(w.name, sched.label())
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic}
@@ -272,6 +287,7 @@ def main():
                    "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "threads": q["threads"],
                    "grid": q["grid"]},
         "roofline": roof,
+        "clock": clock,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(A, B, w, args.cpu_seconds)

@@ -134,6 +134,42 @@ ts_status ts_gemm(const void* A, const void* B, void* C,
                   const ts_schedule* sched, void* stream);
 
 /*
+ * ts_gemm with a clock record, for measurement: the same product, launch and
+ * errors, and in addition thread 0 of every workgroup p writes four counters to
+ * the device buffer clock_out (owned by the caller, clock_rows x 4 uint64):
+ *   clock_out[4p + 0 .. 1] = shader-clock counter (s_memtime) at the start and end
+ *                            of the workgroup,
+ *   clock_out[4p + 2 .. 3] = constant 100 MHz counter (s_memrealtime) at the same
+ *                            two points,
+ * so (end - start) of the first over (end - start) of the second, times 100 MHz,
+ * is the shader clock the workgroup ran at.  Used to state a kernel's MFMA
+ * utilisation at the clock the board's power limit actually allowed.
+ * clock_rows must be >= the launch grid (ts_query), else TS_ERR_INVALID_ARG;
+ * clock_out == NULL is TS_ERR_INVALID_ARG.
+ */
+ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
+                          int64_t M, int64_t N, int64_t K,
+                          int64_t stride_am, int64_t stride_ak,
+                          int64_t stride_bk, int64_t stride_bn,
+                          int64_t stride_cm, int64_t stride_cn,
+                          int32_t ab_dtype, int32_t c_dtype,
+                          const ts_schedule* sched, void* stream,
+                          uint64_t* clock_out, int64_t clock_rows);
+
+/*
+ * Measurement probe: one workgroup of 8 waves per compute unit, each wave running
+ * `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16 with no memory traffic,
+ * enqueued on `stream`.  Times the matrix cores' sustained rate on this device
+ * when the caller brackets it with events: *flops (host pointer) receives the
+ * floating-point operations the launch executes.  `sink` is a caller-owned device
+ * buffer of at least (compute units x 512) floats that receives one value per
+ * thread (the accumulators' sum, so that no MFMA is dead code).
+ * Errors: TS_ERR_INVALID_ARG (iters <= 0, null pointers, sink too small),
+ * TS_ERR_NO_DEVICE, TS_ERR_HIP (launch failure).
+ */
+ts_status ts_mfma_loop_probe(int32_t iters, float* sink, int64_t sink_elems, double* flops, void* stream);
+
+/*
  * Writes the work sequence of every workgroup, computed on the GPU by the same
  * device functions the GEMM kernels use, to the device buffer `out` of
  * out_rows x 5 int32: row (p * max_items + it) = (p, it, tile_m, tile_n, k_step)

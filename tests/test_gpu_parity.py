@@ -5,6 +5,7 @@ plus one unit in the last place of |C*| for 16-bit outputs.  Integer-valued
 inputs make every fp32 accumulation exact, so there the GPU result must equal
 the oracle's exact value rounded to the output type, bit for bit.
 """
+import ctypes
 import itertools
 
 import numpy as np
@@ -253,3 +254,46 @@ def test_deterministic():
     c1 = run(A, B, "f16", "f16", s, 1000, 1100, 700)
     c2 = run(A, B, "f16", "f16", s, 1000, 1100, 700)
     assert torch.equal(c1, c2)
+
+
+# ---- the clocked entry point: same product, plausible clock record -------------------
+
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+def test_gemm_clocked_matches_gemm(mode):
+    M, N, K = 1024, 768, 512
+    A, B = workloads.pair(M, N, K, "f16", "uniform", 777)
+    a, b = to_device(A, "f16"), to_device(B, "f16")
+    s = ts.Schedule(order="grouped", group_m=8, mode=mode, xcd_remap=True)
+    say(f"gemm_clocked {M}x{N}x{K} {s.label()}")
+    c0 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    c1 = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    ts.gemm(a, b, out=c0, schedule=s)
+    rec = ts.gemm_clocked(a, b, c1, schedule=s)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1)
+    grid = ts.query(M, N, K, s)["grid"]
+    assert rec.shape[0] == grid
+    r = rec.cpu()
+    assert bool((r[:, 1] > r[:, 0]).all()) and bool((r[:, 3] > r[:, 2]).all())
+    clk = ts.clock_ghz(rec)
+    say(f"clock {clk}")
+    assert clk["programs"] == grid and 0.3 < clk["mean"] < 3.5
+
+
+def test_gemm_clocked_rejects_short_record():
+    M, N, K = 512, 512, 256
+    a = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    b = torch.zeros((K, N), dtype=torch.float16, device="cuda")
+    c = torch.zeros((M, N), dtype=torch.float16, device="cuda")
+    rec = torch.zeros((1, 4), dtype=torch.int64, device="cuda")
+    s = ts.Schedule(mode="tiled")
+    assert ts.query(M, N, K, s)["grid"] > 1
+    st = ts._lib.ts_gemm_clocked(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, K, 1, N, 1, N, 1,
+                                 ts.TS_F16, ts.TS_F16, ctypes.byref(s._c()), 0, rec.data_ptr(), 1)
+    assert st == ts.TS_ERR_INVALID_ARG
+
+
+def test_mfma_loop_probe_rate():
+    tf = ts.mfma_loop_tflops(iters=4000, reps=2)
+    say(f"mfma loop probe {tf:.1f} TFLOP/s")
+    assert 200.0 < tf < 2600.0   # below the 2.4 GHz dense fp16 figure

@@ -52,6 +52,10 @@ class LaunchInfo(ctypes.Structure):
 
 _lib.ts_gemm.argtypes = [_p, _p, _p] + [_i64] * 9 + [_i32, _i32, ctypes.POINTER(_Schedule), _p]
 _lib.ts_gemm.restype = _i32
+_lib.ts_gemm_clocked.argtypes = _lib.ts_gemm.argtypes + [_p, _i64]
+_lib.ts_gemm_clocked.restype = _i32
+_lib.ts_mfma_loop_probe.argtypes = [_i32, _p, _i64, ctypes.POINTER(ctypes.c_double), _p]
+_lib.ts_mfma_loop_probe.restype = _i32
 _lib.ts_schedule_trace.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule), _p, _i64, _p]
 _lib.ts_schedule_trace.restype = _i32
 _lib.ts_schedule_trace_host.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule),
@@ -62,7 +66,8 @@ _lib.ts_query.restype = _i32
 _lib.ts_status_string.argtypes = [_i32]
 _lib.ts_status_string.restype = ctypes.c_char_p
 
-EXPORTS = ("ts_gemm", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query", "ts_status_string")
+EXPORTS = ("ts_gemm", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
+           "ts_status_string", "ts_mfma_loop_probe")
 
 
 class TsError(RuntimeError):
@@ -132,6 +137,57 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
                       _stream_handle(a.device))
     _check(st)
     return out
+
+
+def gemm_clocked(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, schedule: Schedule | None = None):
+    """ts_gemm_clocked: C = A @ B into ``out`` plus the per-workgroup clock record.
+
+    Returns an int64 [grid, 4] CUDA tensor (shader-clock counter at start and end,
+    100 MHz counter at start and end of every workgroup); use ``clock_ghz`` on it.
+    """
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0] or out.shape != (a.shape[0], b.shape[1]):
+        raise ValueError("shapes do not multiply")
+    M, K = a.shape
+    N = b.shape[1]
+    sched = schedule or Schedule()
+    grid = query(M, N, K, sched, _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0))["grid"]
+    rec = torch.zeros((max(grid, 1), 4), dtype=torch.int64, device=a.device)
+    s = sched._c()
+    _check(_lib.ts_gemm_clocked(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                                a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
+                                _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0), ctypes.byref(s),
+                                _stream_handle(a.device), rec.data_ptr(), rec.shape[0]))
+    return rec
+
+
+def clock_ghz(rec) -> dict:
+    """Shader clock per workgroup from a ts_gemm_clocked record (s_memtime ticks over
+    100 MHz s_memrealtime ticks): mean / min / max over workgroups, in GHz."""
+    r = rec.cpu().to(torch.float64)
+    ticks = r[:, 1] - r[:, 0]
+    secs = (r[:, 3] - r[:, 2]) / 100e6
+    ok = secs > 0
+    ghz = ticks[ok] / secs[ok] / 1e9
+    return {"mean": float(ghz.mean()), "min": float(ghz.min()), "max": float(ghz.max()),
+            "programs": int(ok.sum())}
+
+
+def mfma_loop_tflops(iters: int = 20000, reps: int = 3, device: int | str = "cuda") -> float:
+    """Sustained MFMA rate (TFLOP/s) of the no-memory probe, best of ``reps`` timed launches."""
+    q = query(256, 256, 256)
+    sink = torch.empty(q["cu_count"] * 512, dtype=torch.float32, device=device)
+    flops = ctypes.c_double(0.0)
+    stream = _stream_handle(sink.device)
+    _check(_lib.ts_mfma_loop_probe(iters, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream))
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(_lib.ts_mfma_loop_probe(iters, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream))
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flops.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
 
 
 def gemm_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int,

@@ -193,10 +193,10 @@ extern "C" const char* ts_status_string(ts_status status) {
     return "unknown ts_status";
 }
 
-extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                              int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
                              int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
-                             const ts_schedule* sched, void* stream) {
+                             const ts_schedule* sched, void* stream, uint64_t* clock_out, int64_t clock_rows) {
     Plan p;
     ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
     if (st != TS_OK) return st;
@@ -225,6 +225,7 @@ extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, i
     const int ppc = (p.mode != TS_MODE_TILED && p.requested_programs == 0) ? programs_per_cu(p) : 1;
     st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
     if (st != TS_OK) return st;
+    if (clock_out && clock_rows < p.s.grid) return TS_ERR_INVALID_ARG;
 
     GemmArgs g;
     g.A = static_cast<const uint16_t*>(A);
@@ -240,6 +241,7 @@ extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, i
     g.vec_b = p.vec_b;
     g.vec_c = p.vec_c;
     g.s = p.s;
+    g.clk = reinterpret_cast<unsigned long long*>(clock_out);
     const KernelRef k = kernel_of(p);
     void* args[] = {&g};
     if (hipLaunchKernel(k.fn, dim3(p.s.grid), dim3(k.threads), args, 0, (hipStream_t)stream) != hipSuccess) {
@@ -247,6 +249,24 @@ extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, i
         return TS_ERR_HIP;
     }
     return TS_OK;
+}
+
+extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                             int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                             int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
+                             const ts_schedule* sched, void* stream) {
+    return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       ab_dtype, c_dtype, sched, stream, nullptr, 0);
+}
+
+extern "C" ts_status ts_gemm_clocked(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                     int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                                     int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
+                                     const ts_schedule* sched, void* stream, uint64_t* clock_out,
+                                     int64_t clock_rows) {
+    if (!clock_out) return TS_ERR_INVALID_ARG;
+    return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       ab_dtype, c_dtype, sched, stream, clock_out, clock_rows);
 }
 
 extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,

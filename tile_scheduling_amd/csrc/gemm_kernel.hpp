@@ -69,6 +69,33 @@ struct GemmArgs {
     long long lda, ldb, ldc;  // row strides in elements (inner strides are 1)
     int vec_a, vec_b, vec_c;  // 1 if rows allow 16-byte (A, B) / full-width (C) vectors
     SchedArgs s;
+    unsigned long long* clk;  // null, or 4 values per program (see ProgramClock)
+};
+
+// Optional per-program clock record: shader-clock counter (s_memtime) and the
+// constant 100 MHz counter (s_memrealtime) at the program's start and end, written
+// by thread 0 as clk[4p .. 4p+3] = {shader start, shader end, real start, real end}.
+// The ratio of the two differences is the shader clock the program ran at.
+struct ProgramClock {
+    unsigned long long c0 = 0, r0 = 0;
+    __device__ __forceinline__ void start(const GemmArgs& g) {
+        if (g.clk) {
+            c0 = __builtin_amdgcn_s_memtime();
+            r0 = __builtin_amdgcn_s_memrealtime();
+        }
+    }
+    __device__ __forceinline__ void stop(const GemmArgs& g) {
+        if (g.clk) {
+            const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+            if (threadIdx.x == 0) {
+                unsigned long long* d = g.clk + 4 * (unsigned long long)blockIdx.x;
+                d[0] = c0;
+                d[1] = c1;
+                d[2] = r0;
+                d[3] = r1;
+            }
+        }
+    }
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_>
@@ -916,6 +943,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
     Engine<Cfg, TI, TO, MASKED> e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
+    ProgramClock pc;
+    pc.start(g);
     const ProgramWork w(g.s, blockIdx.x);
     const int ntiles = (MODE == MODE_TILED) ? 1 : w.ntiles;
     for (int i = 0; i < ntiles; ++i) {
@@ -927,6 +956,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
         e.store_tile(m0, n0);
     }
     e.drain();
+    pc.stop(g);
 }
 
 // Position of the flattened loop: cursor plus the origin of its tile.
@@ -958,9 +988,14 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
     typedef Engine<Cfg, TI, TO, MASKED> E;
     E e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
+    ProgramClock pc;
+    pc.start(g);
     const ProgramWork w(g.s, blockIdx.x);
     const int total = w.total_items();
-    if (total == 0) return;
+    if (total == 0) {
+        pc.stop(g);
+        return;
+    }
     FlatPos cp{FlatCursor(w), 0, 0};   // item being multiplied
     cp.template coords<Cfg>(g.s);
     FlatPos p1 = cp;                   // item 1
@@ -1000,6 +1035,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
         }
     }
     e.drain();
+    pc.stop(g);
 }
 
 // Schedule trace: one thread per program, the same functions as above.
