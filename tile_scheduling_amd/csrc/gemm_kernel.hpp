@@ -433,11 +433,21 @@ struct Engine {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     }
 
-    // Scalar-register buffer resource over `p`; zero records when `valid` is false,
-    // which turns every load through it into a zero with no memory access.
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* p, bool valid) const {
+    // Scalar-register buffer resource over `p` with `nrec` records: -1 (all) for a
+    // slice that exists, 0 past the last one, which turns every load through it
+    // into a zero with no memory access.  The count is an integer computed with
+    // scalar arithmetic (see vmask): a select on a bool is materialised in a vector
+    // register, which drags the whole resource into vector registers and makes the
+    // compiler wrap every load in a loop over distinct lane values.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* p, int nrec) const {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
-                                                 __builtin_amdgcn_readfirstlane(valid ? -1 : 0), kBufferFlags);
+                                                 __builtin_amdgcn_readfirstlane(nrec), kBufferFlags);
+    }
+    // -1 if k < lim, else 0 (for 0 <= k, lim < 2^30)
+    static __device__ __forceinline__ int vmask(int k, int lim) {
+        int d = k - lim;
+        asm("" : "+s"(d));  // opaque: keeps the shift from being folded back into a compare and select
+        return d >> 31;
     }
 
     // Fast path: one direct-to-LDS load of 16 bytes per lane; lane l's bytes land at
@@ -453,7 +463,7 @@ struct Engine {
         dma16(r, a_go[((c * NW) >> 2) & 1], (int)((long long)grp * 8 * g.lda * 2), la[SLOT] + grp * 1024);
     }
     template <int SLOT>
-    __device__ __forceinline__ void dma_a(int m0, int k, bool valid) {
+    __device__ __forceinline__ void dma_a(int m0, int k, int valid) {
         const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
 #pragma unroll
         for (int c = 0; c < A_DMA_N; ++c) dma_a_one<SLOT>(c, r);
@@ -465,14 +475,14 @@ struct Engine {
         dma16(r, b_dg[((c * NW * RPD) >> 3) & 1], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
     }
     template <int SLOT>
-    __device__ __forceinline__ void dma_b(int n0, int k, bool valid) {
+    __device__ __forceinline__ void dma_b(int n0, int k, int valid) {
         const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k * BK * g.ldb + n0, valid);
 #pragma unroll
         for (int c = 0; c < B_DMA_N; ++c) dma_b_one<SLOT>(c, r);
     }
 
     // A slice k of tile row m0 into registers (register path).
-    __device__ __forceinline__ void load_a(int m0, int k, bool valid) {
+    __device__ __forceinline__ void load_a(int m0, int k, int valid) {
         const int k0 = k * BK;
         if (!MASKED) {
             const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k0, valid);
@@ -505,7 +515,7 @@ struct Engine {
 
     // B slice k of tile column n0 into register set SET.
     template <int SET>
-    __device__ __forceinline__ void load_b(int n0, int k, bool valid) {
+    __device__ __forceinline__ void load_b(int n0, int k, int valid) {
         const int k0 = k * BK;
         if (!MASKED) {
             const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k0 * g.ldb + n0, valid);
@@ -626,12 +636,12 @@ struct Engine {
 
     // Slices loaded by a K step: A slice ka of tile row origin m0 (DA slices ahead
     // of the one multiplied) and B slice kb of tile column origin n0 (DB ahead).
-    // A false `v*` means past the last slice: nothing is read and zeros flow.
+    // A zero `v*` means past the last slice: nothing is read and zeros flow.
     struct Next {
         int m0, ka;
-        bool va;
+        int va;    // record-count mask: -1 for a slice that exists, 0 past the last
         int n0, kb;
-        bool vb;
+        int vb;
     };
 
     // Issue plan of the unmasked paths over the MFMA slots of a K step (global slot
@@ -791,13 +801,21 @@ struct Engine {
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // Fast path: the fragments of the first two sub-steps of slot SLOT, as the
+    // last two sub-steps of the K step before read them.
+    template <int SLOT>
+    __device__ __forceinline__ void reread_frags() {
+        read_frags<SLOT>(0, 0);
+        read_frags<SLOT>(1, 1);
+    }
+
     // Prologue: slice p0 in slot 0 with the fragments of its first sub-step read
     // (fast path: of its first two); the fast path also has slice p1 in flight
     // into slot 1.  The first K step then loads the slices after.
     __device__ __forceinline__ void prologue(const Next& p0, const Next& p1) {
         if constexpr (FAST) {
-            dma_b<0>(p0.n0, p0.kb, true);
-            dma_a<0>(p0.m0, p0.ka, true);
+            dma_b<0>(p0.n0, p0.kb, -1);
+            dma_a<0>(p0.m0, p0.ka, -1);
             dma_b<1>(p1.n0, p1.kb, p1.vb);
             dma_a<1>(p1.m0, p1.ka, p1.va);
             barrier_after_loads<B_DMA_N + A_DMA_N>();
@@ -805,8 +823,8 @@ struct Engine {
             read_frags<0>(1, 1);
             return;
         } else {
-            load_b<0>(p0.n0, p0.kb, true);
-            load_a(p0.m0, p0.ka, true);
+            load_b<0>(p0.n0, p0.kb, -1);
+            load_a(p0.m0, p0.ka, -1);
             store_a<0>();
             store_b<0, 0>();
             __syncthreads();
@@ -824,9 +842,9 @@ struct Engine {
     // Full pipeline for one tile (no epilogue): steps alternate B slots 0 and 1; an
     // odd step count runs one slot-0 step first and then pairs starting on slot 1.
     __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
-        prologue(Next{m0, 0, true, n0, 0, true}, Next{m0, 1, ks > 1, n0, 1, ks > 1});
+        prologue(Next{m0, 0, -1, n0, 0, -1}, Next{m0, 1, vmask(1, ks), n0, 1, vmask(1, ks)});
         auto nx = [&](int k) {  // loads of step k
-            return Next{m0, k + DA, k + DA < ks, n0, k + DB, k + DB < ks};
+            return Next{m0, k + DA, vmask(k + DA, ks), n0, k + DB, vmask(k + DB, ks)};
         };
         int k = 0;
         if (ks & 1) {
@@ -861,7 +879,13 @@ struct Engine {
     static __device__ __forceinline__ int stage_swz(int r) { return (CPR == 8 ? (r >> 1) : r) & (CPR - 1); }
 
     __device__ __forceinline__ void store_tile_staged(int m0, int n0) {
-        const int r32 = lane & 31, hk = lane >> 5;
+        // The lane index passes through an opaque copy here, so the per-lane
+        // addresses below are formed at the store; otherwise, where the epilogue sits
+        // inside a K loop, they are hoisted out of it and held in registers through
+        // every step.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int r32 = ln & 31, hk = ln >> 5;
         char* st = ldsc + wave * Cfg::STAGE_W;
         OutT* C = reinterpret_cast<OutT*>(g.C);
 #pragma unroll
@@ -886,7 +910,7 @@ struct Engine {
                 }
 #pragma unroll
                 for (int u = 0; u < Cfg::STAGE_W / 1024; ++u) {
-                    const int off = u * 1024 + lane * 16;
+                    const int off = u * 1024 + ln * 16;
                     const int row = off / ROWB, ch = (off % ROWB) >> 4;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * ROWB + ((ch ^ stage_swz(row)) << 4));
                     const long long m = m0 + wm * Cfg::TM + i * 32 + h * RS + row;
@@ -1000,8 +1024,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     cp.template coords<Cfg>(g.s);
     FlatPos p1 = cp;                   // item 1
     p1.template advance<Cfg>(g.s, w);
-    e.prologue(typename E::Next{cp.m0, cp.c.k, true, cp.n0, cp.c.k, true},
-               typename E::Next{p1.m0, p1.c.k, total > 1, p1.n0, p1.c.k, total > 1});
+    e.prologue(typename E::Next{cp.m0, cp.c.k, -1, cp.n0, cp.c.k, -1},
+               typename E::Next{p1.m0, p1.c.k, E::vmask(1, total), p1.n0, p1.c.k, E::vmask(1, total)});
     FlatPos ld = p1;                   // next item whose slices are loaded (DA = DB ahead)
     static_assert(E::DA == E::DB, "one load cursor");
     if (E::DA == 2) ld.template advance<Cfg>(g.s, w);
@@ -1012,11 +1036,16 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     auto step = [&](auto slot_tag) {
         constexpr int SLOT = decltype(slot_tag)::value;
         if (cp.c.k == 0) e.zero_acc();
-        e.template kstep<SLOT>(typename E::Next{ld.m0, ld.c.k, it + E::DA < total, ld.n0, ld.c.k, it + E::DA < total},
-                               stored);
+        const int vm = E::vmask(it + E::DA, total);
+        e.template kstep<SLOT>(typename E::Next{ld.m0, ld.c.k, vm, ld.n0, ld.c.k, vm}, stored);
         ld.template advance<Cfg>(g.s, w);
         stored = cp.c.last_k(w);
-        if (stored) e.store_tile(cp.m0, cp.n0);
+        if (stored) {
+            e.store_tile(cp.m0, cp.n0);
+            // fast path: the fragments the step read ahead are dropped and read
+            // again after the epilogue, which then runs with none of them held
+            if constexpr (E::FAST) e.template reread_frags<SLOT ^ 1>();
+        }
         cp.template advance<Cfg>(g.s, w);
         ++it;
     };
