@@ -111,14 +111,33 @@ def time_gemm(ts, torch, a, b, c, sched, steps, warmup):
     wall = time.perf_counter() - t0
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return {"wall_s": wall, "event_ms": ev[0].elapsed_time(ev[-1]) / steps, "median_ms": per[len(per) // 2],
-            "min_ms": per[0], "max_ms": per[-1]}
+            "min_ms": per[0], "p90_ms": per[min(steps - 1, (9 * steps) // 10)], "max_ms": per[-1]}
 
 
-def cpu_baseline(A, B, w, budget_s: float):
+def time_gemm_cold(ts, torch, a, b, c, sched, steps, flush):
+    """Per-launch event times with a 1 GiB write between launches (evicts the L2s and
+    the Infinity Cache); the events bracket the GEMM alone."""
+    stream = torch.cuda.current_stream()
+    ts.gemm(a, b, out=c, schedule=sched)
+    per = []
+    for i in range(steps):
+        flush.fill_(float(i & 7))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ts.gemm(a, b, out=c, schedule=sched)
+        e1.record(stream)
+        per.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in per)
+    return {"median_ms": t[len(t) // 2], "min_ms": t[0], "p90_ms": t[min(steps - 1, (9 * steps) // 10)],
+            "max_ms": t[-1]}
+
+
+def cpu_baseline(A, B, w, budget_s: float, threads: int = 0):
     """The oracle on whole rows of C, sized to about budget_s seconds of host work."""
     from oracle import gemm as og
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
     rows = threads
     t0 = time.perf_counter()
     og.gemm(A, B, w.ab_dtype, rows=(0, rows), threads=threads)
@@ -194,6 +213,58 @@ def ksweep(ts, torch, np, workloads, steps):
         del a, b, c
 
 
+EXTRA_SETS = (
+    # (workload, schedules): the 8192 grid, every order x mode on the ragged bf16 shape,
+    # and one GPU's share of an eight-way row split of the headline product
+    ("gemm_8192x8192x4096_f16", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped8") for r in ("", "+remap")
+                                 for m in ("tiled", "persistent", "crosstile")]),
+    ("gemm_5000x12290x1000_bf16_f32", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped4", "grouped8", "grouped16")
+                                       for r in ("", "+remap") for m in ("tiled", "persistent", "crosstile")]),
+    ("gemm_2048x16384x4096_f16_mshare8", [f"{o}/{m}" for o in ("rowmajor", "grouped8+remap")
+                                          for m in ("tiled", "persistent", "crosstile")]),
+)
+
+
+def extras(ts, torch, np, workloads, a, b, c, w, sched, steps):
+    """Supplementary tables on stderr: hot and cold-cache timing of the benchmarked
+    launch, the other workloads' schedules (useful and executed TFLOP/s), and the
+    oracle on one host thread."""
+    flops = 2.0 * w.M * w.N * w.K
+    flush = torch.empty(1 << 29, dtype=torch.float16, device="cuda")
+    hot = time_gemm(ts, torch, a, b, c, sched, steps, 3)
+    cold = time_gemm_cold(ts, torch, a, b, c, sched, steps, flush)
+    for name, r in (("hot", hot), ("cold", cold)):
+        log(f"extras {w.name} {sched.label()} {name:4s} median {r['median_ms']:.4f} ms "
+            f"(min {r['min_ms']:.4f}, p90 {r['p90_ms']:.4f}, max {r['max_ms']:.4f})  "
+            f"{flops / r['median_ms'] / 1e9:8.1f} TFLOP/s")
+    del flush
+    by_name = {x.name: x for x in workloads.ALL}
+    for name, labels in EXTRA_SETS:
+        x = by_name[name]
+        A, B = workloads.inputs(x)
+        in_dtype = torch.float16 if x.ab_dtype == "f16" else torch.bfloat16
+        out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[x.c_dtype]
+        xa = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
+        xb = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
+        xc = torch.empty((x.M, x.N), dtype=out_dtype, device="cuda")
+        useful = 2.0 * x.M * x.N * x.K
+        for lab in labels:
+            s = parse_schedule(lab)
+            q = ts.query(x.M, x.N, x.K, s, ts.TS_F16 if x.ab_dtype == "f16" else ts.TS_BF16,
+                         {"f16": ts.TS_F16, "bf16": ts.TS_BF16, "f32": ts.TS_F32}[x.c_dtype])
+            executed = 2.0 * (q["num_m_tiles"] * q["block_m"]) * (q["num_n_tiles"] * q["block_n"]) * \
+                (q["k_steps"] * q["block_k"])
+            r = time_gemm(ts, torch, xa, xb, xc, s, steps, 3)
+            t = r["median_ms"] * 1e-3
+            log(f"extras {x.name} {lab:28s} tile {q['block_m']}x{q['block_n']}x{q['block_k']} grid {q['grid']:5d}  "
+                f"median {r['median_ms']:.4f} ms (p90 {r['p90_ms']:.4f})  {useful / t / 1e12:7.1f} TFLOP/s useful  "
+                f"{executed / t / 1e12:7.1f} executed")
+        del xa, xb, xc
+    A, B = workloads.inputs(w)
+    one = cpu_baseline(A, B, w, 3.0, threads=1)
+    log(f"extras oracle one thread: {one['value'] * 1e3:.3f} GFLOP/s ({one['sample']})")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +275,9 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
     ap.add_argument("--ksweep", action="store_true",
                     help="also time persistent vs cross-tile over the K sweep (table on stderr)")
+    ap.add_argument("--extras", action="store_true",
+                    help="also print hot/cold timing, the other workloads' schedules and the "
+                         "one-thread oracle rate (tables on stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-target", action="store_true",
@@ -212,7 +286,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the GEMM is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "(the GEMM runs on one GPU; a multi-GPU split by rows of A and C is not built)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -237,6 +311,8 @@ def main():
 
     if args.ksweep:
         ksweep(ts, torch, np, workloads, max(10, args.steps))
+    if args.extras:
+        extras(ts, torch, np, workloads, a, b, c, w, parse_schedule(args.schedule), max(10, args.steps))
     if args.sweep:
         labels = []
         for order in ("rowmajor", "grouped4", "grouped8", "grouped16"):
@@ -258,7 +334,7 @@ def main():
     value = flops * args.steps / r["wall_s"] / 1e12
     achieved = flops / (r["event_ms"] * 1e-3) / 1e12
     log(f"timed {args.steps} steps: wall {ms_per_step:.4f} ms/step, events {r['event_ms']:.4f} ms/launch "
-        f"(median {r['median_ms']:.4f}, min {r['min_ms']:.4f}, max {r['max_ms']:.4f})")
+        f"(median {r['median_ms']:.4f}, min {r['min_ms']:.4f}, p90 {r['p90_ms']:.4f}, max {r['max_ms']:.4f})")
 
     # One more launch with the per-workgroup clock record, outside the timed region:
     # the shader clock the board's power limit allowed, and the MFMA peak at it.

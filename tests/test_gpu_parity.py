@@ -116,6 +116,26 @@ def test_ragged_every_schedule(tile, ab, c_dtype):
             assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
 
 
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("ab,c_dtype", IO)
+def test_ragged_word_aligned_rows(tile, ab, c_dtype):
+    # K = 6 and N = 2 (mod 8): A and B rows are 4-byte but not 16-byte aligned, and
+    # so are C rows of 16-bit outputs (fp32 rows are 8-byte aligned); the masked
+    # loads and stores then move 4-byte pieces
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    M, N, K = 2 * bm + 5, 3 * bn + 2, 4 * bk + 6
+    A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 610)
+    C, S = og.gemm(A, B, ab, threads=4)
+    first = None
+    for sched in schedules(tile, P=5):
+        c = run(A, B, ab, c_dtype, sched, M, N, K)
+        if first is None:
+            first = c
+            assert_accept(to_f64(c), C, S, c_dtype, sched.label())
+        else:
+            assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
+
+
 # ---- the ragged bf16 workload at full size: all four schedules -----------------------
 
 def test_ragged_bf16_5000x12290x1000_full_size():
@@ -183,6 +203,13 @@ def test_16384x16384x4096_sampled():
     _large(workloads.SQ_16384, [ts.Schedule(order=o, group_m=g, mode=m, xcd_remap=r)
                                 for (o, g) in (("row_major", 8), ("grouped", 4), ("grouped", 8), ("grouped", 16))
                                 for m in ("tiled", "persistent", "crosstile") for r in (False, True)])
+
+
+def test_m_share_2048x16384x4096_sampled():
+    # one GPU's share of an eight-way row split of the 16384 x 16384 x 4096 product
+    _large(workloads.SHARE_M8, [ts.Schedule(order=o, group_m=8, mode=m, xcd_remap=r)
+                                for (o, r) in (("row_major", False), ("grouped", True))
+                                for m in ("tiled", "persistent", "crosstile")])
 
 
 @pytest.mark.parametrize("w", workloads.K_SWEEP[:4], ids=lambda w: w.name)

@@ -133,11 +133,11 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     p->s.grid = 0;
     // dense, 16-byte aligned operands assumed until ts_gemm sees the real ones
     const int64_t c_elem = c == TS_F32 ? 4 : 2;
-    p->vec_a = (K % 8) == 0;
-    p->vec_b = (N % 8) == 0;
-    p->vec_c = (N * c_elem) % 16 == 0;
+    p->vec_a = (K % 8) == 0 ? 2 : (K % 2) == 0 ? 1 : 0;
+    p->vec_b = (N % 8) == 0 ? 2 : (N % 2) == 0 ? 1 : 0;
+    p->vec_c = (N * c_elem) % 16 == 0 ? 2 : (N * c_elem) % 8 == 0 ? 1 : 0;
     p->masked = (M % p->bm) != 0 || (N % p->bn) != 0 || (K % p->bk) != 0 || K == 0 ||
-                !p->vec_a || !p->vec_b || !p->vec_c;
+                p->vec_a != 2 || p->vec_b != 2 || p->vec_c != 2;
     return TS_OK;
 }
 
@@ -211,12 +211,16 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     const int c_elem = c_dtype == TS_F32 ? 4 : 2;
     if ((a & 1) || (b & 1) || (c % c_elem)) return TS_ERR_ALIGNMENT;
 
-    // 16-byte operand vectors need 16-byte aligned rows; C vectors are 4 elements.
-    p.vec_a = (a % 16 == 0) && (stride_am % 8 == 0 || M == 1);
-    p.vec_b = (b % 16 == 0) && (stride_bk % 8 == 0 || K <= 1);
-    p.vec_c = (c % (4 * c_elem) == 0) && (stride_cm % 4 == 0 || M == 1);
-    p.masked = (M % p.bm) != 0 || (N % p.bn) != 0 || (K % p.bk) != 0 || K == 0 || !p.vec_a || !p.vec_b ||
-               !p.vec_c;
+    // Alignment levels of the rows: 16-byte operand vectors need 16-byte aligned
+    // rows, 4-byte pieces 4-byte aligned ones; C vectors are 4 elements, pieces 2.
+    p.vec_a = (a % 16 == 0) && (stride_am % 8 == 0 || M == 1) ? 2
+              : (a % 4 == 0) && (stride_am % 2 == 0 || M == 1) ? 1 : 0;
+    p.vec_b = (b % 16 == 0) && (stride_bk % 8 == 0 || K <= 1) ? 2
+              : (b % 4 == 0) && (stride_bk % 2 == 0 || K <= 1) ? 1 : 0;
+    p.vec_c = (c % (4 * c_elem) == 0) && (stride_cm % 4 == 0 || M == 1) ? 2
+              : (c % (2 * c_elem) == 0) && (stride_cm % 2 == 0 || M == 1) ? 1 : 0;
+    p.masked = (M % p.bm) != 0 || (N % p.bn) != 0 || (K % p.bk) != 0 || K == 0 || p.vec_a != 2 ||
+               p.vec_b != 2 || p.vec_c != 2;
 
     int dev;
     DeviceInfo di;

@@ -67,7 +67,10 @@ struct GemmArgs {
     void* C;
     int M, N, K;
     long long lda, ldb, ldc;  // row strides in elements (inner strides are 1)
-    int vec_a, vec_b, vec_c;  // 1 if rows allow 16-byte (A, B) / full-width (C) vectors
+    // Row alignment of A, B (16-bit elements) and C: 2 if rows allow 16-byte (A, B) /
+    // full 4-element (C) vectors, 1 if they allow 4-byte (A, B) / 2-element (C) pieces,
+    // 0 if only single elements.
+    int vec_a, vec_b, vec_c;
     SchedArgs s;
     unsigned long long* clk;  // null, or 4 values per program (see ProgramClock)
 };
@@ -149,9 +152,12 @@ __device__ __forceinline__ uint32_t pack_bits(uint16_t lo, uint16_t hi) { return
 template <class TO> struct Out;
 template <> struct Out<OutF32> {
     typedef float T;
-    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, bool vec) {
-        if (vec && valid >= 4) {
+    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, int vec) {
+        if (vec >= 2 && valid >= 4) {
             *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (vec == 1 && valid >= 4) {
+            reinterpret_cast<float2*>(p)[0] = make_float2(v[0], v[1]);
+            reinterpret_cast<float2*>(p)[1] = make_float2(v[2], v[3]);
         } else {
             for (int e = 0; e < 4; ++e) if (e < valid) p[e] = v[e];
         }
@@ -159,13 +165,18 @@ template <> struct Out<OutF32> {
 };
 template <> struct Out<OutF16> {
     typedef _Float16 T;
-    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, bool vec) {
+    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, int vec) {
         _Float16 h[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-        if (vec && valid >= 4) {
+        if (vec >= 1 && valid >= 4) {
             u32x2 w;
             w[0] = pack_bits(__builtin_bit_cast(uint16_t, h[0]), __builtin_bit_cast(uint16_t, h[1]));
             w[1] = pack_bits(__builtin_bit_cast(uint16_t, h[2]), __builtin_bit_cast(uint16_t, h[3]));
-            *reinterpret_cast<u32x2*>(p) = w;
+            if (vec >= 2) {
+                *reinterpret_cast<u32x2*>(p) = w;
+            } else {
+                reinterpret_cast<uint32_t*>(p)[0] = w[0];
+                reinterpret_cast<uint32_t*>(p)[1] = w[1];
+            }
         } else {
             for (int e = 0; e < 4; ++e) if (e < valid) p[e] = h[e];
         }
@@ -173,13 +184,18 @@ template <> struct Out<OutF16> {
 };
 template <> struct Out<OutBF16> {
     typedef __bf16 T;
-    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, bool vec) {
+    static __device__ __forceinline__ void store4(T* p, const float* v, int valid, int vec) {
         __bf16 h[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        if (vec && valid >= 4) {
+        if (vec >= 1 && valid >= 4) {
             u32x2 w;
             w[0] = pack_bits(__builtin_bit_cast(uint16_t, h[0]), __builtin_bit_cast(uint16_t, h[1]));
             w[1] = pack_bits(__builtin_bit_cast(uint16_t, h[2]), __builtin_bit_cast(uint16_t, h[3]));
-            *reinterpret_cast<u32x2*>(p) = w;
+            if (vec >= 2) {
+                *reinterpret_cast<u32x2*>(p) = w;
+            } else {
+                reinterpret_cast<uint32_t*>(p)[0] = w[0];
+                reinterpret_cast<uint32_t*>(p)[1] = w[1];
+            }
         } else {
             for (int e = 0; e < 4; ++e) if (e < valid) p[e] = h[e];
         }
@@ -187,8 +203,15 @@ template <> struct Out<OutBF16> {
 };
 
 // 8 consecutive 16-bit elements p[0..7], those at or past `valid` read as zero.
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int valid, bool vec) {
-    if (vec && valid >= 8) return *reinterpret_cast<const u32x4*>(p);
+// `vec` is the alignment level of p (2: 16 bytes, 1: 4 bytes, 0: 2 bytes).
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int valid, int vec) {
+    if (valid >= 8) {
+        if (vec >= 2) return *reinterpret_cast<const u32x4*>(p);
+        if (vec == 1) {
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+            return u32x4{q[0], q[1], q[2], q[3]};
+        }
+    }
     uint32_t e[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) e[q] = (q < valid) ? (uint32_t)p[q] : 0u;
