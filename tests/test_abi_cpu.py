@@ -94,6 +94,10 @@ def test_query_tile_grid_and_masking():
     assert q["grid"] == 256 and q["masked"] == 1
     q = ts.query(16384, 16384, 4096, ts.Schedule())
     assert (q["block_m"], q["num_tiles"], q["masked"]) == (256, 4096, 0)
+    # rows too long for 32-bit in-tile offsets of the unmasked kernels: masked path
+    assert ts.query(256, 256, 1 << 22, ts.Schedule(tile="256x256x64"))["masked"] == 1
+    assert ts.query(256, 1 << 25, 64, ts.Schedule(tile="256x256x64"))["masked"] == 1
+    assert ts.query(256, 256, 1 << 21, ts.Schedule(tile="256x256x64"))["masked"] == 0
     q = ts.query(64, 64, 0, ts.Schedule(mode="crosstile", num_programs=8))
     assert q["k_steps"] == 0 and q["masked"] == 1  # K = 0 still writes C (zeros)
 

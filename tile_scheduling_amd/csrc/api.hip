@@ -137,7 +137,8 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     p->vec_b = (N % 8) == 0 ? 2 : (N % 2) == 0 ? 1 : 0;
     p->vec_c = (N * c_elem) % 16 == 0 ? 2 : (N * c_elem) % 8 == 0 ? 1 : 0;
     p->masked = (M % p->bm) != 0 || (N % p->bn) != 0 || (K % p->bk) != 0 || K == 0 ||
-                p->vec_a != 2 || p->vec_b != 2 || p->vec_c != 2;
+                p->vec_a != 2 || p->vec_b != 2 || p->vec_c != 2 ||
+                (int64_t)p->bm * K * 2 > INT_MAX || (int64_t)p->bk * N * 2 > INT_MAX;
     return TS_OK;
 }
 
@@ -221,6 +222,9 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
               : (c % (2 * c_elem) == 0) && (stride_cm % 2 == 0 || M == 1) ? 1 : 0;
     p.masked = (M % p.bm) != 0 || (N % p.bn) != 0 || (K % p.bk) != 0 || K == 0 || p.vec_a != 2 ||
                p.vec_b != 2 || p.vec_c != 2;
+    // The unmasked kernels form row offsets inside a tile as 32-bit byte counts; the
+    // masked ones use full-width pointers.
+    if ((int64_t)p.bm * stride_am * 2 > INT_MAX || (int64_t)p.bk * stride_bk * 2 > INT_MAX) p.masked = 1;
 
     int dev;
     DeviceInfo di;
