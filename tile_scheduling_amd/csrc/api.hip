@@ -248,6 +248,12 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     g.vec_a = p.vec_a;
     g.vec_b = p.vec_b;
     g.vec_c = p.vec_c;
+    {
+        const int64_t pitch = stride_cm * c_elem;
+        int ca = 16;
+        while (ca > 2 && ((c % ca) != 0 || (M > 1 && pitch % ca != 0))) ca >>= 1;
+        g.c_align = ca;
+    }
     g.s = p.s;
     g.clk = reinterpret_cast<unsigned long long*>(clock_out);
     const KernelRef k = kernel_of(p);

@@ -71,6 +71,7 @@ struct GemmArgs {
     // full 4-element (C) vectors, 1 if they allow 4-byte (A, B) / 2-element (C) pieces,
     // 0 if only single elements.
     int vec_a, vec_b, vec_c;
+    int c_align;              // largest of 16, 8, 4, 2 bytes dividing C's base and row pitch
     SchedArgs s;
     unsigned long long* clk;  // null, or 4 values per program (see ProgramClock)
 };
@@ -884,21 +885,55 @@ struct Engine {
         }
     }
 
-    // Fast-path epilogue: each wave converts RS rows of its sub-tile at a time into
+    // Epilogue of the BK = 64 tiles (fast and masked): each wave converts RS rows of its sub-tile at a time into
     // its own 4 KiB of LDS ([row][TN] of the output type, 16-byte chunks XOR-
     // swizzled by row so that the column writes and the row reads are free of bank
     // conflicts) and writes them back to C as whole row segments: lane l of a
     // 16-byte store covers chunk l mod CPR of row l / CPR, so a store instruction
     // writes 1 KiB of complete rows.  Lanes of a 32-row block whose row is not in
-    // the current group skip the LDS write.
+    // the current group skip the LDS write.  The masked kernels skip rows past M,
+    // write the columns before N of a chunk that crosses N one by one, and split
+    // whole chunks into pieces of the alignment C's rows allow.
     typedef typename Out<TO>::T OutT;
     static constexpr int OSZ = sizeof(OutT);
     static constexpr int ROWB = Cfg::TN * OSZ;                  // bytes of one sub-tile row
     static constexpr int CPR = ROWB / 16;                       // 16-byte chunks per row
     static constexpr int RS = Cfg::STAGE_W / ROWB;              // rows per staging round
     static constexpr int NST = FAST ? FM * (32 / RS) * (Cfg::STAGE_W / 1024) : 0;  // stores per tile
-    static_assert(!FAST || (RS >= 1 && 32 % RS == 0 && (CPR == 8 || CPR == 16 || CPR == 32 || CPR == 64)),
+    static constexpr bool STAGED = Cfg::C_BYTES > 0;
+    static_assert(!STAGED || (RS >= 1 && 32 % RS == 0 && (CPR == 8 || CPR == 16 || CPR == 32 || CPR == 64)),
                   "staging shape");
+    static_assert(!FAST || STAGED, "the fast path stages its epilogue");
+
+    // One 16-byte chunk v of row segment p (its columns n .. n + 16/OSZ - 1, of which
+    // `valid` are before N) to C, masked path.
+    __device__ __forceinline__ void store_chunk_masked(char* p, const u32x4& v, int valid) const {
+        constexpr int E = 16 / OSZ;
+        if (valid >= E) {
+            if (g.c_align >= 16) {
+                *reinterpret_cast<u32x4*>(p) = v;
+            } else if (g.c_align >= 8) {
+                reinterpret_cast<u32x2*>(p)[0] = u32x2{v[0], v[1]};
+                reinterpret_cast<u32x2*>(p)[1] = u32x2{v[2], v[3]};
+            } else if (g.c_align >= 4) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) reinterpret_cast<uint32_t*>(p)[w] = v[w];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (e < valid) {
+                    if (OSZ == 4)
+                        reinterpret_cast<uint32_t*>(p)[e] = v[e];
+                    else
+                        reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+    }
     static __device__ __forceinline__ int stage_swz(int r) { return (CPR == 8 ? (r >> 1) : r) & (CPR - 1); }
 
     __device__ __forceinline__ void store_tile_staged(int m0, int n0) {
@@ -937,7 +972,12 @@ struct Engine {
                     const int row = off / ROWB, ch = (off % ROWB) >> 4;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * ROWB + ((ch ^ stage_swz(row)) << 4));
                     const long long m = m0 + wm * Cfg::TM + i * 32 + h * RS + row;
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(C + m * g.ldc + n0 + wn * Cfg::TN) + ch * 16) = v;
+                    char* dst = reinterpret_cast<char*>(C + m * g.ldc + n0 + wn * Cfg::TN) + ch * 16;
+                    if (!MASKED) {
+                        *reinterpret_cast<u32x4*>(dst) = v;
+                    } else if (m < g.M) {
+                        store_chunk_masked(dst, v, g.N - (n0 + wn * Cfg::TN + ch * (16 / OSZ)));
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -946,7 +986,7 @@ struct Engine {
 
     // Accumulators -> C (round to the output type), masked to M x N.
     __device__ __forceinline__ void store_tile(int m0, int n0) {
-        if constexpr (FAST) {
+        if constexpr (STAGED) {
             store_tile_staged(m0, n0);
             return;
         }
