@@ -91,7 +91,12 @@ def test_query_tile_grid_and_masking():
     q = ts.query(5000, 12290, 1000, ts.Schedule(mode="persistent", num_programs=256, tile="256x256x64"),
                  ts.TS_BF16, ts.TS_F32)
     assert (q["num_m_tiles"], q["num_n_tiles"], q["k_steps"]) == (20, 49, 16)
-    assert q["grid"] == 256 and q["masked"] == 1
+    assert q["grid"] == 256 and q["masked"] == 3   # edge path, B rows in 4-byte pieces
+    # kernel path: whole tiles 0, masked registers 1, zero-filled edges 2 (16-byte B) or 3 (4-byte B)
+    assert ts.query(1000, 1024, 512, ts.Schedule(tile="256x256x64"))["masked"] == 2
+    assert ts.query(1000, 1025, 512, ts.Schedule(tile="256x256x64"))["masked"] == 1   # N odd
+    assert ts.query(1000, 1024, 500, ts.Schedule(tile="256x256x64"))["masked"] == 1   # K not 0 mod 8
+    assert ts.query(1000, 1024, 512, ts.Schedule(tile="64x64x32"))["masked"] == 1     # no direct-to-LDS tile
     q = ts.query(16384, 16384, 4096, ts.Schedule())
     assert (q["block_m"], q["num_tiles"], q["masked"]) == (256, 4096, 0)
     # rows too long for 32-bit in-tile offsets of the unmasked kernels: masked path

@@ -136,6 +136,42 @@ def test_ragged_word_aligned_rows(tile, ab, c_dtype):
             assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
 
 
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("ab,c_dtype", IO)
+@pytest.mark.parametrize("n_tail", [8, 2], ids=["edge16", "edge4"])
+def test_ragged_edge_paths(tile, ab, c_dtype, n_tail):
+    # K a multiple of 8 with a partial last slice, M and N ragged: the direct-to-LDS
+    # tiles zero-fill the edges (B in 16-byte pieces when N = 0 mod 8, else 4-byte);
+    # the 64-wide tile has no such pipeline and runs masked
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    M, N, K = 2 * bm + 5, 3 * bn + n_tail, 4 * bk + 8
+    expect_path = 1 if tile == "64x64x32" else (2 if n_tail == 8 else 3)
+    assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == expect_path
+    A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 620)
+    C, S = og.gemm(A, B, ab, threads=4)
+    first = None
+    for sched in schedules(tile, P=5):
+        c = run(A, B, ab, c_dtype, sched, M, N, K)
+        if first is None:
+            first = c
+            assert_accept(to_f64(c), C, S, c_dtype, sched.label())
+        else:
+            assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
+
+
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+def test_edge_path_integer_inputs_bit_exact(tile):
+    # exact integer products: any wrong or missing element (a tail chunk not zeroed,
+    # a row past M read, a column past N stored) shows as a mismatch
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    for (M, N, K) in ((bm + 1, bn + 2, bk + 8), (3 * bm - 7, 2 * bn + 8, 2 * bk + 56), (17, 30, 8)):
+        A, B = workloads.pair(M, N, K, "f16", "int", 630)
+        C, _ = og.gemm(A, B, "f16")
+        for mode in ("tiled", "persistent", "crosstile"):
+            got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode=mode, num_programs=3, tile=tile), M, N, K))
+            assert np.array_equal(got, C), (M, N, K, mode)
+
+
 # ---- the ragged bf16 workload at full size: all four schedules -----------------------
 
 def test_ragged_bf16_5000x12290x1000_full_size():
@@ -152,7 +188,8 @@ def test_ragged_bf16_5000x12290x1000_full_size():
                   ts.Schedule(order="grouped", group_m=8, mode="tiled", xcd_remap=True, tile="256x256x64w8"),
                   ts.Schedule(order="grouped", group_m=8, mode="crosstile", tile="256x256x64w8")]:
         q = ts.query(w.M, w.N, w.K, sched, ts.TS_BF16, ts.TS_F32)
-        assert q["masked"] == 1 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
+        # edges zero-filled by the direct-to-LDS loads, B's 4-byte aligned rows in 4-byte pieces
+        assert q["masked"] == 3 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
         c = run(A, B, w.ab_dtype, w.c_dtype, sched, w.M, w.N, w.K)
         if base is None:
             base = c

@@ -56,7 +56,8 @@ struct Plan {
     int bm, bn, bk;
     int io;                 // IO_*
     int mode;
-    bool masked;
+    bool masked;            // the tiles do not cover M x N x K exactly, or rows defeat 16-byte access
+    int path;               // PATH_*: which kernel runs a masked plan
     int vec_a, vec_b, vec_c;
     SchedArgs s;            // grid filled once the device is known (persistent auto)
     int requested_programs; // 0 = auto
@@ -74,11 +75,36 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
 
 KernelRef kernel_of(const Plan& p) {
     switch (p.cfg) {
-        case CFG_64: return kernels_cfg64(p.io, p.masked, p.mode);
-        case CFG_128: return kernels_cfg128(p.io, p.masked, p.mode);
-        case CFG_256W8: return kernels_cfg256w8(p.io, p.masked, p.mode);
-        default: return kernels_cfg256(p.io, p.masked, p.mode);
+        case CFG_64: return kernels_cfg64(p.io, p.path, p.mode);
+        case CFG_128: return kernels_cfg128(p.io, p.path, p.mode);
+        case CFG_256W8: return kernels_cfg256w8(p.io, p.path, p.mode);
+        default: return kernels_cfg256(p.io, p.path, p.mode);
     }
+}
+
+bool cfg_has_fast_path(int cfg) {
+    switch (cfg) {
+        case CFG_64: return has_fast_path<Cfg64>();
+        case CFG_128: return has_fast_path<Cfg128>();
+        case CFG_256W8: return has_fast_path<Cfg256w8>();
+        default: return has_fast_path<Cfg256>();
+    }
+}
+
+// Kernel path of a plan.  A masked plan runs the direct-to-LDS pipeline with
+// zero-filled edges when every load of it lies wholly inside or wholly outside
+// A and B: A's base 16-byte aligned with K and its row stride multiples of 8
+// elements; B's base, row stride and N multiples of 16 bytes (16-byte loads) or of
+// 4 bytes (4-byte loads); and the in-tile offsets below 2^30 bytes.  Otherwise the
+// masked register pipeline runs.
+int choose_path(const Plan& p, int64_t N, int64_t K, uintptr_t a, uintptr_t b, int64_t lda, int64_t ldb) {
+    if (!p.masked) return PATH_FULL;
+    if (!cfg_has_fast_path(p.cfg) || K <= 0 || K % 8 != 0) return PATH_MASKED;
+    if (a % 16 != 0 || lda % 8 != 0) return PATH_MASKED;
+    if ((int64_t)p.bm * lda * 2 >= (1LL << 30) || (int64_t)p.bk * ldb * 2 >= (1LL << 30)) return PATH_MASKED;
+    if (b % 16 == 0 && ldb % 8 == 0 && N % 8 == 0) return PATH_EDGE16;
+    if (b % 4 == 0 && ldb % 2 == 0 && N % 2 == 0) return PATH_EDGE4;
+    return PATH_MASKED;
 }
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -139,6 +165,7 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     p->masked = (M % p->bm) != 0 || (N % p->bn) != 0 || (K % p->bk) != 0 || K == 0 ||
                 p->vec_a != 2 || p->vec_b != 2 || p->vec_c != 2 ||
                 (int64_t)p->bm * K * 2 > INT_MAX || (int64_t)p->bk * N * 2 > INT_MAX;
+    p->path = choose_path(*p, N, K, 0, 0, K, N);
     return TS_OK;
 }
 
@@ -225,6 +252,7 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     // The unmasked kernels form row offsets inside a tile as 32-bit byte counts; the
     // masked ones use full-width pointers.
     if ((int64_t)p.bm * stride_am * 2 > INT_MAX || (int64_t)p.bk * stride_bk * 2 > INT_MAX) p.masked = 1;
+    p.path = choose_path(p, N, K, a, b, stride_am, stride_bk);
 
     int dev;
     DeviceInfo di;
@@ -254,6 +282,8 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
         while (ca > 2 && ((c % ca) != 0 || (M > 1 && pitch % ca != 0))) ca >>= 1;
         g.c_align = ca;
     }
+    g.a_bytes = K > 0 ? ((M - 1) * stride_am + K) * 2 : 0;
+    g.b_bytes = K > 0 ? ((K - 1) * stride_bk + N) * 2 : 0;
     g.s = p.s;
     g.clk = reinterpret_cast<unsigned long long*>(clock_out);
     const KernelRef k = kernel_of(p);
@@ -309,7 +339,7 @@ extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
     out->cu_count = have_dev ? di.cu_count : 0;
     out->xcds = p.s.xcds;
     out->lds_bytes = k.lds_bytes;
-    out->masked = p.masked ? 1 : 0;
+    out->masked = p.path;
     out->vgprs = -1;
     out->scratch_bytes = -1;
     if (have_dev) {

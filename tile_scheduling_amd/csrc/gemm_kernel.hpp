@@ -72,6 +72,7 @@ struct GemmArgs {
     // 0 if only single elements.
     int vec_a, vec_b, vec_c;
     int c_align;              // largest of 16, 8, 4, 2 bytes dividing C's base and row pitch
+    long long a_bytes, b_bytes;  // bytes from A (B) to the end of its last element
     SchedArgs s;
     unsigned long long* clk;  // null, or 4 values per program (see ProgramClock)
 };
@@ -270,8 +271,15 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //  register (masked edges, or BK = 32): A and B one slice ahead in registers,
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
-template <class Cfg, class TI, class TO, bool MASKED>
+// Kernel paths: whole tiles; masked register pipeline; direct-to-LDS pipeline with
+// ragged edges, its B loads 16 bytes (EDGE16) or 4 bytes (EDGE4) per lane.
+enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE16 = 2, PATH_EDGE4 = 3 };
+
+template <class Cfg, class TI, class TO, int PATH>
 struct Engine {
+    static constexpr bool MASKED = PATH == PATH_MASKED;
+    static constexpr bool EDGE = PATH == PATH_EDGE16 || PATH == PATH_EDGE4;
+    static constexpr bool EDGES = PATH != PATH_FULL;   // C stores masked to M x N
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH, SUB = Cfg::SUB;
     static constexpr int CA = Cfg::CA, CB = Cfg::CB, KBH = Cfg::KBH;
@@ -282,11 +290,16 @@ struct Engine {
     static constexpr int NBN = BN / 8;               // B loader blocks along n
     static constexpr int RBB = BN * 2;               // bytes of one [k][n] B row (fast path)
     static constexpr int LPR = RBB / 16, RPD = 64 / LPR;   // B load lanes per row, rows per 1 KiB load
-    static constexpr bool FAST = !MASKED && RB == 128 && Cfg::C_BYTES > 0 && (BM * RB) % (1024 * NW) == 0 &&
-                                 LPR >= 16 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
-                                 (BK * RBB) % (1024 * NW) == 0 && (NW * RPD) % 8 == 0;
+    static constexpr bool FAST_OK = RB == 128 && Cfg::C_BYTES > 0 && (BM * RB) % (1024 * NW) == 0 &&
+                                    LPR >= 16 && LPR <= 64 && (LPR & (LPR - 1)) == 0 &&
+                                    (BK * RBB) % (1024 * NW) == 0 && (NW * RPD) % 8 == 0 &&
+                                    (BK * (RBB / 256)) % NW == 0;
+    static constexpr bool FAST = !MASKED && FAST_OK;
+    static_assert(!EDGE || FAST, "the edge paths run the direct-to-LDS pipeline");
+    static constexpr int BH = RBB / 256;                                // 256-byte pieces of a B row
     static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
-    static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
+    static constexpr int B_DMA_N = !FAST ? 0 : PATH == PATH_EDGE4 ? BK * BH / NW   // 256-byte B loads per wave
+                                                                  : BK * RBB / 1024 / NW;  // 1 KiB B loads per wave
     static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
     static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
     static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
@@ -312,6 +325,8 @@ struct Engine {
     uint32_t b_sel[2];    // register path: byte-permute selector of B writes with even / odd j
     // per-lane global byte offsets
     uint32_t a_go[2], b_go;   // A: [c&1] of the load / chunk index c
+    uint32_t a_kc[2];         // edge paths: first k (element) of the A chunk a_go[e] points at
+    int klim = 0;             // edge paths: k elements of the A slice being loaded that exist
     bool b_active;        // this thread owns a B loader block
 
     u32x4 ra[FAST ? 1 : CA];                 // A slice in flight (register path)
@@ -352,6 +367,7 @@ struct Engine {
             for (int e = 0; e < 2; ++e) {
                 const int grp7 = (4 * e + wave) & 7;
                 a_go[e] = (uint32_t)(((long long)row * g.lda + ((pc ^ row ^ grp7) * 8)) * 2);
+                a_kc[e] = (uint32_t)((pc ^ row ^ grp7) * 8);
                 a_wr[e] = 0;
             }
             // B: [k][n] rows whose 16-byte chunks are XOR-swizzled by
@@ -480,27 +496,74 @@ struct Engine {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff, soff, 0, 0);
     }
 
-    // Fast path: 1 KiB A load number c of this wave, into A slot `slot`.
+    // Buffer resource over the slice at element offset `off` of A (B): on the edge
+    // paths its record count stops at the matrix's last element, so that rows past
+    // M (K) and columns past the end read as zero.  Every offset of those loads is
+    // in the per-lane offset, which the range check covers, and every load lies
+    // wholly inside or wholly outside the range (the edge paths need K, lda and the
+    // base (N, ldb and the base) to be multiples of the load size).
+    // The count is clamped to [0, 2^31 - 16], a multiple of every load size; the
+    // in-tile offsets of the edge paths stay below 2^30.
+    static __device__ __forceinline__ int clamp_records(long long left) {
+        return (int)(left < 0 ? 0 : left < 0x7ffffff0LL ? left : 0x7ffffff0LL);
+    }
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_a(long long off, int valid) const {
+        if constexpr (!EDGE) return rsrc(g.A + off, valid);
+        return rsrc(g.A + off, clamp_records(g.a_bytes - 2 * off) & valid);
+    }
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(long long off, int valid) const {
+        if constexpr (!EDGE) return rsrc(g.B + off, valid);
+        return rsrc(g.B + off, clamp_records(g.b_bytes - 2 * off) & valid);
+    }
+    // A per-lane offset no record count reaches: the load reads zero.
+    static constexpr uint32_t kOutOfRange = 0x80000000u;
+
+    // Fast path: 1 KiB A load number c of this wave, into A slot `slot`.  Edge
+    // paths: chunks at or past k = klim of the slice read as zero.
     template <int SLOT>
     __device__ __forceinline__ void dma_a_one(int c, const __amdgpu_buffer_rsrc_t& r) {
         const int grp = c * NW + wave;                     // 8-row group (1 KiB)
-        dma16(r, a_go[((c * NW) >> 2) & 1], (int)((long long)grp * 8 * g.lda * 2), la[SLOT] + grp * 1024);
+        const int e = ((c * NW) >> 2) & 1;
+        if constexpr (EDGE) {
+            const uint32_t voff = a_go[e] + (uint32_t)(grp * 8 * (int)g.lda * 2);
+            dma16(r, (int)a_kc[e] < klim ? voff : kOutOfRange, 0, la[SLOT] + grp * 1024);
+        } else {
+            dma16(r, a_go[e], (int)((long long)grp * 8 * g.lda * 2), la[SLOT] + grp * 1024);
+        }
     }
     template <int SLOT>
     __device__ __forceinline__ void dma_a(int m0, int k, int valid) {
-        const __amdgpu_buffer_rsrc_t r = rsrc(g.A + (long long)m0 * g.lda + k * BK, valid);
+        const __amdgpu_buffer_rsrc_t r = rsrc_a((long long)m0 * g.lda + k * BK, valid);
+        if constexpr (EDGE) klim = g.K - k * BK;
 #pragma unroll
         for (int c = 0; c < A_DMA_N; ++c) dma_a_one<SLOT>(c, r);
     }
-    // Fast path: 1 KiB B load number c of this wave, into B slot `slot`.
+    // Fast path: B load number c of this wave, into B slot `slot`: 1 KiB (16 bytes a
+    // lane), or on PATH_EDGE4 256 bytes (4 bytes a lane) of one row, placed in the
+    // same swizzled image: lane l's dword lands at byte 4 l of its 256-byte piece,
+    // i.e. in chunk l/4 of the piece, which holds logical chunk (l/4) ^ f(k).
     template <int SLOT>
     __device__ __forceinline__ void dma_b_one(int c, const __amdgpu_buffer_rsrc_t& r) {
-        const int grp = c * NW + wave;                     // RPD-row group (1 KiB)
-        dma16(r, b_dg[((c * NW * RPD) >> 3) & 1], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
+        if constexpr (PATH == PATH_EDGE4) {
+            const int idx = c * NW + wave;                 // 256-byte piece of the slice
+            const int kr = idx / BH, h = idx % BH;          // its row and its place in the row
+            const int f = (4 * (kr & 3)) ^ (2 * ((kr >> 3) & 1));
+            const uint32_t voff = (((uint32_t)lane * 4) ^ (uint32_t)(16 * f)) + (uint32_t)(h * 256) +
+                                  (uint32_t)(kr * (int)g.ldb * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(lb[SLOT] + kr * RBB + h * 256), 4, (int)voff, 0, 0, 0);
+        } else {
+            const int grp = c * NW + wave;                 // RPD-row group (1 KiB)
+            const int e = ((c * NW * RPD) >> 3) & 1;
+            if constexpr (EDGE)
+                dma16(r, b_dg[e] + (uint32_t)(grp * RPD * (int)g.ldb * 2), 0, lb[SLOT] + grp * 1024);
+            else
+                dma16(r, b_dg[e], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
+        }
     }
     template <int SLOT>
     __device__ __forceinline__ void dma_b(int n0, int k, int valid) {
-        const __amdgpu_buffer_rsrc_t r = rsrc(g.B + (long long)k * BK * g.ldb + n0, valid);
+        const __amdgpu_buffer_rsrc_t r = rsrc_b((long long)k * BK * g.ldb + n0, valid);
 #pragma unroll
         for (int c = 0; c < B_DMA_N; ++c) dma_b_one<SLOT>(c, r);
     }
@@ -776,7 +839,7 @@ struct Engine {
     // this slice freed: B (slice nx.kb), then A (slice nx.ka), into slot SLOT.
     static constexpr int F_NFR = FM + FN;                            // fragment reads per sub-step
     static constexpr int F_DS = 2 * NMF >= 2 * NVM ? 2 : 1;          // MFMA slots between loads
-    static_assert(!FAST || 2 * NMF >= NVM, "loads must fit the two sub-steps after the barrier");
+    static constexpr int F_PER = (NVM + 2 * NMF - 1) / (2 * NMF);    // loads per such slot
     template <int SLOT, int S>
     __device__ __forceinline__ void fast_sub(const __amdgpu_buffer_rsrc_t& ra_, const __amdgpu_buffer_rsrc_t& rb_) {
         constexpr int RS = (S + 2) & 3;
@@ -788,12 +851,15 @@ struct Engine {
             if (t < F_NFR) read_frag<RSLOT>(RS, t, RS);
             if (S >= 2) {
                 const int gt = (S - 2) * NMF + t;
-                const int vi = gt / F_DS;
-                if (gt % F_DS == 0 && vi < NVM) {
-                    if (vi < B_DMA_N)
-                        dma_b_one<SLOT>(vi, rb_);
-                    else
-                        dma_a_one<SLOT>(vi - B_DMA_N, ra_);
+                if (gt % F_DS == 0) {
+#pragma unroll
+                    for (int d = 0; d < F_PER; ++d) {
+                        const int vi = (gt / F_DS) * F_PER + d;
+                        if (vi < B_DMA_N)
+                            dma_b_one<SLOT>(vi, rb_);
+                        else if (vi < NVM)
+                            dma_a_one<SLOT>(vi - B_DMA_N, ra_);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -801,15 +867,17 @@ struct Engine {
     }
 
     // `after_store`: the epilogue stores of the tile before were issued after the
-    // loads this barrier waits for; they may stay in flight.
+    // loads this barrier waits for; they may stay in flight.  Not on the edge paths:
+    // their masked epilogue issues a varying number of stores, so they wait for all.
     template <int SLOT>
     __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false) {
         if constexpr (FAST) {
-            const __amdgpu_buffer_rsrc_t rb_ = rsrc(g.B + (long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
-            const __amdgpu_buffer_rsrc_t ra_ = rsrc(g.A + (long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b((long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a((long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            if constexpr (EDGE) klim = g.K - nx.ka * BK;
             fast_sub<SLOT, 0>(ra_, rb_);
             fast_sub<SLOT, 1>(ra_, rb_);
-            if (after_store)
+            if (!EDGE && after_store)
                 barrier_after_loads<(NST < 63 ? NST : 63)>();
             else
                 barrier_after_loads<0>();
@@ -973,7 +1041,7 @@ struct Engine {
                     const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * ROWB + ((ch ^ stage_swz(row)) << 4));
                     const long long m = m0 + wm * Cfg::TM + i * 32 + h * RS + row;
                     char* dst = reinterpret_cast<char*>(C + m * g.ldc + n0 + wn * Cfg::TN) + ch * 16;
-                    if (!MASKED) {
+                    if (!EDGES) {
                         *reinterpret_cast<u32x4*>(dst) = v;
                     } else if (m < g.M) {
                         store_chunk_masked(dst, v, g.N - (n0 + wn * Cfg::TN + ch * (16 / OSZ)));
@@ -1024,12 +1092,12 @@ struct Engine {
 
 // Tiled and persistent modes: for each of the program's tiles, a full pipeline
 // (prologue loads, K loop with two slices in flight, epilogue).
-template <class Cfg, class TI, class TO, bool MASKED, int MODE>
+template <class Cfg, class TI, class TO, int PATH, int MODE>
 __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
-    Engine<Cfg, TI, TO, MASKED> e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
+    Engine<Cfg, TI, TO, PATH> e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
     ProgramClock pc;
     pc.start(g);
     const ProgramWork w(g.s, blockIdx.x);
@@ -1039,7 +1107,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
         tile_coords(g.s, w.tile_id(i), tm, tn);
         const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
         e.zero_acc();
-        if (!MASKED || g.s.ks > 0) e.tile_mainloop(m0, n0, g.s.ks);
+        if (PATH != PATH_MASKED || g.s.ks > 0) e.tile_mainloop(m0, n0, g.s.ks);
         e.store_tile(m0, n0);
     }
     e.drain();
@@ -1068,12 +1136,12 @@ struct FlatPos {
 // Flattened cross-tile mode: one loop over (tile, k) items.  The slices of the
 // next items -- the first slices of the next tile when item it ends a tile -- are
 // in flight while item it is multiplied and, at a tile's last K step, stored.
-template <class Cfg, class TI, class TO, bool MASKED>
+template <class Cfg, class TI, class TO, int PATH>
 __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
-    typedef Engine<Cfg, TI, TO, MASKED> E;
+    typedef Engine<Cfg, TI, TO, PATH> E;
     E e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
     ProgramClock pc;
     pc.start(g);

@@ -24,31 +24,51 @@ struct KernelRef {
     int lds_bytes;   // static LDS of the instance
 };
 
-template <class Cfg, class TI, class TO, bool MK>
+template <class Cfg, class TI, class TO, int PATH>
 const void* kernel_by_mode(int mode) {
     switch (mode) {
-        case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, MK, MODE_TILED>);
-        case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, MK, MODE_PERSISTENT>);
-        default: return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, MK>);
+        case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_TILED>);
+        case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_PERSISTENT>);
+        default: return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);
+    }
+}
+
+template <class Cfg, class TI, class TO>
+const void* kernel_by_path(int path, int mode) {
+    // configurations without the direct-to-LDS pipeline run their edges masked
+    constexpr bool fast = Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK;
+    switch (path) {
+        case PATH_FULL: return kernel_by_mode<Cfg, TI, TO, PATH_FULL>(mode);
+        case PATH_EDGE16:
+            if constexpr (fast) return kernel_by_mode<Cfg, TI, TO, PATH_EDGE16>(mode);
+            return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
+        case PATH_EDGE4:
+            if constexpr (fast) return kernel_by_mode<Cfg, TI, TO, PATH_EDGE4>(mode);
+            return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
+        default: return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
     }
 }
 
 template <class Cfg>
-KernelRef kernel_for(int io, bool masked, int mode) {
+KernelRef kernel_for(int io, int path, int mode) {
     const void* f = nullptr;
     switch (io) {
-        case IO_F16_F16: f = masked ? kernel_by_mode<Cfg, InF16, OutF16, true>(mode) : kernel_by_mode<Cfg, InF16, OutF16, false>(mode); break;
-        case IO_F16_F32: f = masked ? kernel_by_mode<Cfg, InF16, OutF32, true>(mode) : kernel_by_mode<Cfg, InF16, OutF32, false>(mode); break;
-        case IO_BF16_BF16: f = masked ? kernel_by_mode<Cfg, InBF16, OutBF16, true>(mode) : kernel_by_mode<Cfg, InBF16, OutBF16, false>(mode); break;
-        default: f = masked ? kernel_by_mode<Cfg, InBF16, OutF32, true>(mode) : kernel_by_mode<Cfg, InBF16, OutF32, false>(mode); break;
+        case IO_F16_F16: f = kernel_by_path<Cfg, InF16, OutF16>(path, mode); break;
+        case IO_F16_F32: f = kernel_by_path<Cfg, InF16, OutF32>(path, mode); break;
+        case IO_BF16_BF16: f = kernel_by_path<Cfg, InBF16, OutBF16>(path, mode); break;
+        default: f = kernel_by_path<Cfg, InBF16, OutF32>(path, mode); break;
     }
     return KernelRef{f, Cfg::NT, Cfg::LDS_BYTES};
 }
 
+// Whether a configuration has the direct-to-LDS pipeline (and so the edge paths).
+template <class Cfg>
+constexpr bool has_fast_path() { return Engine<Cfg, InF16, OutF16, PATH_FULL>::FAST_OK; }
+
 // One function per tile configuration, each defined in its own translation unit.
-KernelRef kernels_cfg64(int io, bool masked, int mode);
-KernelRef kernels_cfg128(int io, bool masked, int mode);
-KernelRef kernels_cfg256(int io, bool masked, int mode);
-KernelRef kernels_cfg256w8(int io, bool masked, int mode);
+KernelRef kernels_cfg64(int io, int path, int mode);
+KernelRef kernels_cfg128(int io, int path, int mode);
+KernelRef kernels_cfg256(int io, int path, int mode);
+KernelRef kernels_cfg256w8(int io, int path, int mode);
 
 }  // namespace ts

@@ -1,7 +1,7 @@
 // Kernel instances of the 128-wide tile configuration (every mode, type pair and
-// masking variant).
+// path).
 #include "internal.hpp"
 
 namespace ts {
-KernelRef kernels_cfg128(int io, bool masked, int mode) { return kernel_for<Cfg128>(io, masked, mode); }
+KernelRef kernels_cfg128(int io, int path, int mode) { return kernel_for<Cfg128>(io, path, mode); }
 }  // namespace ts
