@@ -104,7 +104,11 @@ typedef struct {
     int32_t cu_count;                   /* compute units of the current device (0 if none)    */
     int32_t xcds;                       /* XCDs the workgroups are dealt over (8 if no device) */
     int32_t lds_bytes;                  /* LDS per workgroup                                   */
-    int32_t masked;                     /* 1 = edge-masked kernel variant (ragged or unaligned) */
+    int32_t masked;                     /* kernel path: 0 whole tiles; 1 masked register        */
+                                        /* pipeline (ragged or unaligned); 2 / 3 direct-to-LDS  */
+                                        /* pipeline with zero-filled edges, B loaded in 16- /   */
+                                        /* 4-byte pieces.  ts_query assumes dense, 16-byte      */
+                                        /* aligned operands.                                    */
     int32_t vgprs;                      /* registers per thread reported by the runtime (-1 if none) */
     int32_t scratch_bytes;              /* private (spill) bytes per thread (-1 if none)       */
 } ts_launch_info;
@@ -119,7 +123,10 @@ typedef struct {
  *   M == 0 or N == 0: nothing to do, TS_OK.  K == 0: C is set to zero.
  *   Ragged M, N, K and row strides that defeat 16-byte vector access are handled
  *   by masked loads and stores (out-of-range A and B elements read as zero; C is
- *   written only inside M x N).  sched == NULL means row-major tiled, auto tile.
+ *   written only inside M x N).  When K and A's row stride are multiples of 8
+ *   elements with A 16-byte aligned, and B's base, row stride and N allow 16- or
+ *   4-byte pieces, the edges are zero-filled by the direct-to-LDS loads themselves
+ *   (no element-wise masking).  sched == NULL means row-major tiled, auto tile.
  *   The result does not depend on the schedule: every schedule with the same tile
  *   configuration produces bit-identical C.
  *   Errors: TS_ERR_INVALID_ARG / TS_ERR_UNSUPPORTED / TS_ERR_ALIGNMENT before any
