@@ -193,6 +193,27 @@ def pmc_target(ts, torch, np, workloads):
         del a, b, c
 
 
+STALL_SCHEDULES = ("grouped8+remap/persistent/256x256x64w8", "grouped8+remap/persistent/256x256x64",
+                   "grouped8+remap/crosstile/256x256x64w8")
+
+
+def stall_target(ts, torch, np, workloads):
+    """Launch sequence for the wave-state counter passes: three launches each of the
+    8-wave and 4-wave 256x256x64 persistent kernels and the 8-wave cross-tile kernel
+    at 16384 x 16384 x 4096.  Prints a manifest line per dispatch."""
+    w = workloads.SQ_16384
+    A, B = workloads.inputs(w)
+    a = torch.from_numpy(A.view(np.int16)).view(torch.float16).cuda()
+    b = torch.from_numpy(B.view(np.int16)).view(torch.float16).cuda()
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    for lab in STALL_SCHEDULES:
+        s = parse_schedule(lab)
+        for rep in range(3):
+            ts.gemm(a, b, out=c, schedule=s)
+            torch.cuda.synchronize()
+            print(f"dispatch gemm {w.name} {s.label()} rep{rep}", flush=True)
+
+
 KSWEEP_SCHEDULES = ("grouped8+remap/persistent", "grouped8+remap/crosstile")
 
 
@@ -282,6 +303,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-target", action="store_true",
                     help="run the fixed launch sequence used for hardware-counter passes and exit")
+    ap.add_argument("--stall-target", action="store_true",
+                    help="run the launch sequence of the wave-state counter passes and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -298,6 +321,9 @@ def main():
     by_name = {w.name: w for w in workloads.ALL}
     if args.pmc_target:
         pmc_target(ts, torch, np, workloads)
+        return
+    if args.stall_target:
+        stall_target(ts, torch, np, workloads)
         return
     w = by_name[args.workload]
     out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.c_dtype]
