@@ -244,7 +244,8 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 
 // Two pipelines feed the MFMAs of a K step (64 MFMAs per wave for the big tiles):
 //
-//  fast (unmasked, BK = 64, 128- or 256-wide tiles).  Both operands go straight
+//  fast (BK = 64, 128- or 256-wide tiles; whole tiles, or ragged edges that the
+//    loads zero-fill themselves, see rsrc_a).  Both operands go straight
 //    from global memory into LDS with direct-to-LDS buffer loads, no registers
 //    in between:
 //      A ([m][k], 16-byte chunks swizzled by swz(r) below) into two slots;
@@ -268,7 +269,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //    every global store writes whole 128- or 256-byte row segments.  2 x 32 KiB
 //    of A, 2 x 32 KiB of B and 8 x 4 KiB of staging fill the 160 KiB of LDS of
 //    the 256 x 256 x 64 tile.
-//  register (masked edges, or BK = 32): A and B one slice ahead in registers,
+//  register (other masked shapes, or BK = 32): A and B one slice ahead in registers,
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
 // Kernel paths: whole tiles; masked register pipeline; direct-to-LDS pipeline with
