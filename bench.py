@@ -9,11 +9,16 @@ dense fp16 MFMA peak, from HIP events on the launch stream), the HBM traffic the
 last hardware-counter profile measured for this kernel source, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME] [--sweep] [--ksweep]
+    python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME]
+                    [--sweep] [--ksweep] [--extras] [--pmc-target | --stall-target]
 
 --sweep times every order x remap x mode at the workload; --ksweep times the
 grouped persistent loop against the flattened cross-tile loop over the K sweep
-at 16384 x 16384 (tables on stderr, before the JSON line).
+at 16384 x 16384; --extras times the benchmarked launch hot and cold, the 8192
+grid, the ragged bf16 workload and one GPU's share of an eight-way row split,
+and the oracle on one host thread (tables on stderr, before the JSON line).
+--pmc-target and --stall-target only run the fixed launch sequences that the
+hardware-counter passes profile.
 
 Schedules are written order[+remap]/mode[/P<programs>][/tile], e.g.
 "grouped8+remap/tiled", "rowmajor/persistent/P256", "grouped8/crosstile".
