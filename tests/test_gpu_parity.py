@@ -312,6 +312,32 @@ def test_padded_and_unaligned_operands_with_canaries(tile):
         assert (guard == -12345.0).all(), "write outside C"
 
 
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("N", [296, 290], ids=["edge16", "edge4"])
+def test_edge_paths_padded_operands_with_canaries(tile, N):
+    # padded row strides (8 elements) on the zero-filled-edge paths: the loads stop at
+    # each matrix's last element, the stores stay inside C
+    M, K, pad = 333, 152, 8
+    A, B = workloads.pair(M, N, K, "bf16", "int", 73)
+    C, _ = og.gemm(A, B, "bf16")
+    abuf = torch.full((M, K + pad), 7.0, dtype=torch.bfloat16, device="cuda")
+    bbuf = torch.full((K, N + pad), 7.0, dtype=torch.bfloat16, device="cuda")
+    a, b = abuf[:, :K], bbuf[:, :N]
+    a.copy_(to_device(A, "bf16"))
+    b.copy_(to_device(B, "bf16"))
+    cbuf = torch.full((M + 4, N + 2 * pad + 2), -12345.0, device="cuda")
+    c = cbuf[2:2 + M, pad:pad + N]
+    for mode in ("tiled", "persistent", "crosstile"):
+        say(f"edge canaries {tile} N={N} {mode}")
+        ts.gemm(a, b, out=c, schedule=ts.Schedule(order="grouped", group_m=2, mode=mode, num_programs=3,
+                                                  tile=tile))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(c), C), mode
+        guard = cbuf.clone()
+        guard[2:2 + M, pad:pad + N] = -12345.0
+        assert (guard == -12345.0).all(), "write outside C"
+
+
 def test_deterministic():
     A, B = workloads.pair(1000, 1100, 700, "f16", "uniform", 72)
     s = ts.Schedule(order="grouped", group_m=4, mode="crosstile", xcd_remap=True)
