@@ -967,7 +967,7 @@ struct Engine {
     static constexpr int OSZ = sizeof(OutT);
     static constexpr int ROWB = Cfg::TN * OSZ;                  // bytes of one sub-tile row
     static constexpr int CPR = ROWB / 16;                       // 16-byte chunks per row
-    static constexpr int RS = Cfg::STAGE_W / ROWB;              // rows per staging round
+    static constexpr int RS = Cfg::STAGE_W / ROWB;              // rows per staging pass
     static constexpr int NST = FAST ? FM * (32 / RS) * (Cfg::STAGE_W / 1024) : 0;  // stores per tile
     static constexpr bool STAGED = Cfg::C_BYTES > 0;
     static_assert(!STAGED || (RS >= 1 && 32 % RS == 0 && (CPR == 8 || CPR == 16 || CPR == 32 || CPR == 64)),
@@ -1019,7 +1019,7 @@ struct Engine {
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int h = 0; h < 32 / RS; ++h) {
-                const int r = r32 - h * RS;   // row within this round
+                const int r = r32 - h * RS;   // row within this pass
                 if (r >= 0 && r < RS) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
