@@ -241,13 +241,15 @@ def ksweep(ts, torch, np, workloads, steps):
 
 EXTRA_SETS = (
     # (workload, schedules): the 8192 grid, every order x mode on the ragged bf16 shape,
-    # and one GPU's share of an eight-way row split of the headline product
+    # one GPU's share of an eight-way row split of the headline product, and 4096 cubed
     ("gemm_8192x8192x4096_f16", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped8") for r in ("", "+remap")
                                  for m in ("tiled", "persistent", "crosstile")]),
     ("gemm_5000x12290x1000_bf16_f32", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped4", "grouped8", "grouped16")
                                        for r in ("", "+remap") for m in ("tiled", "persistent", "crosstile")]),
     ("gemm_2048x16384x4096_f16_mshare8", [f"{o}/{m}" for o in ("rowmajor", "grouped8+remap")
                                           for m in ("tiled", "persistent", "crosstile")]),
+    ("gemm_4096x4096x4096_f16", [f"{o}/{m}" for o in ("rowmajor", "grouped8+remap") for m in ("tiled", "persistent")]
+     + ["grouped8+remap/crosstile", "grouped8+remap/tiled/128x128x64", "grouped8+remap/persistent/128x128x64"]),
 )
 
 

@@ -249,6 +249,12 @@ def test_m_share_2048x16384x4096_sampled():
                                 for m in ("tiled", "persistent", "crosstile")])
 
 
+def test_4096_cubed_sampled():
+    _large(workloads.SQ_4096, [ts.Schedule(order=o, group_m=8, mode=m, xcd_remap=r, tile=t)
+                               for (o, r) in (("row_major", False), ("grouped", True))
+                               for m in ("tiled", "persistent", "crosstile") for t in ("auto",)])
+
+
 @pytest.mark.parametrize("w", workloads.K_SWEEP[:4], ids=lambda w: w.name)
 def test_k_sweep_sampled(w):
     _large(w, [ts.Schedule(order="grouped", group_m=8, mode="persistent", xcd_remap=True),

@@ -82,7 +82,10 @@ RAGGED_BF16 = Workload("gemm_5000x12290x1000_bf16_f32", 5000, 12290, 1000, "bf16
 # One GPU's share of the 16384 x 16384 x 4096 product split eight ways by rows of A and C.
 SHARE_M8 = Workload("gemm_2048x16384x4096_f16_mshare8", 2048, 16384, 4096, "f16", "f16", "uniform", 1005)
 
-ALL = (SQUARE_256, SQ_8192, SQ_16384) + K_SWEEP + (RAGGED_BF16, SHARE_M8)
+# The 4096-cubed product the grouped-ordering page also measures.
+SQ_4096 = Workload("gemm_4096x4096x4096_f16", 4096, 4096, 4096, "f16", "f16", "uniform", 1006)
+
+ALL = (SQUARE_256, SQ_8192, SQ_16384) + K_SWEEP + (RAGGED_BF16, SHARE_M8, SQ_4096)
 
 
 def inputs(w: Workload):
