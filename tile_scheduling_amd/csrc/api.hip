@@ -74,11 +74,12 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
 }
 
 KernelRef kernel_of(const Plan& p) {
+    const bool edge = p.path == PATH_EDGE16 || p.path == PATH_EDGE4;   // only on direct-to-LDS tiles
     switch (p.cfg) {
-        case CFG_64: return kernels_cfg64(p.io, p.path, p.mode);
-        case CFG_128: return kernels_cfg128(p.io, p.path, p.mode);
-        case CFG_256W8: return kernels_cfg256w8(p.io, p.path, p.mode);
-        default: return kernels_cfg256(p.io, p.path, p.mode);
+        case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, p.mode);
+        case CFG_128: return edge ? kernels_cfg128_edge(p.io, p.path, p.mode) : kernels_cfg128(p.io, p.path, p.mode);
+        case CFG_256W8: return edge ? kernels_cfg256w8_edge(p.io, p.path, p.mode) : kernels_cfg256w8(p.io, p.path, p.mode);
+        default: return edge ? kernels_cfg256_edge(p.io, p.path, p.mode) : kernels_cfg256(p.io, p.path, p.mode);
     }
 }
 

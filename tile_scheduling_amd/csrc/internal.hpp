@@ -33,30 +33,37 @@ const void* kernel_by_mode(int mode) {
     }
 }
 
+// Whole-tile and masked-register instances (one translation unit per tile
+// configuration) and zero-filled-edge instances (a second one), so that the
+// configurations compile in parallel in halves.
 template <class Cfg, class TI, class TO>
-const void* kernel_by_path(int path, int mode) {
-    // configurations without the direct-to-LDS pipeline run their edges masked
-    constexpr bool fast = Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK;
-    switch (path) {
-        case PATH_FULL: return kernel_by_mode<Cfg, TI, TO, PATH_FULL>(mode);
-        case PATH_EDGE16:
-            if constexpr (fast) return kernel_by_mode<Cfg, TI, TO, PATH_EDGE16>(mode);
-            return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
-        case PATH_EDGE4:
-            if constexpr (fast) return kernel_by_mode<Cfg, TI, TO, PATH_EDGE4>(mode);
-            return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
-        default: return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
-    }
+const void* kernel_by_path_base(int path, int mode) {
+    return path == PATH_FULL ? kernel_by_mode<Cfg, TI, TO, PATH_FULL>(mode)
+                             : kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
+}
+template <class Cfg, class TI, class TO>
+const void* kernel_by_path_edge(int path, int mode) {
+    static_assert(Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK, "edge paths need the direct-to-LDS pipeline");
+    return path == PATH_EDGE16 ? kernel_by_mode<Cfg, TI, TO, PATH_EDGE16>(mode)
+                               : kernel_by_mode<Cfg, TI, TO, PATH_EDGE4>(mode);
 }
 
-template <class Cfg>
+template <class Cfg, class TI, class TO, bool EDGE>
+const void* kernel_by_path(int path, int mode) {
+    if constexpr (EDGE)
+        return kernel_by_path_edge<Cfg, TI, TO>(path, mode);
+    else
+        return kernel_by_path_base<Cfg, TI, TO>(path, mode);
+}
+
+template <class Cfg, bool EDGE>
 KernelRef kernel_for(int io, int path, int mode) {
     const void* f = nullptr;
     switch (io) {
-        case IO_F16_F16: f = kernel_by_path<Cfg, InF16, OutF16>(path, mode); break;
-        case IO_F16_F32: f = kernel_by_path<Cfg, InF16, OutF32>(path, mode); break;
-        case IO_BF16_BF16: f = kernel_by_path<Cfg, InBF16, OutBF16>(path, mode); break;
-        default: f = kernel_by_path<Cfg, InBF16, OutF32>(path, mode); break;
+        case IO_F16_F16: f = kernel_by_path<Cfg, InF16, OutF16, EDGE>(path, mode); break;
+        case IO_F16_F32: f = kernel_by_path<Cfg, InF16, OutF32, EDGE>(path, mode); break;
+        case IO_BF16_BF16: f = kernel_by_path<Cfg, InBF16, OutBF16, EDGE>(path, mode); break;
+        default: f = kernel_by_path<Cfg, InBF16, OutF32, EDGE>(path, mode); break;
     }
     return KernelRef{f, Cfg::NT, Cfg::LDS_BYTES};
 }
@@ -66,9 +73,14 @@ template <class Cfg>
 constexpr bool has_fast_path() { return Engine<Cfg, InF16, OutF16, PATH_FULL>::FAST_OK; }
 
 // One function per tile configuration, each defined in its own translation unit.
+// path PATH_FULL or PATH_MASKED
 KernelRef kernels_cfg64(int io, int path, int mode);
 KernelRef kernels_cfg128(int io, int path, int mode);
 KernelRef kernels_cfg256(int io, int path, int mode);
 KernelRef kernels_cfg256w8(int io, int path, int mode);
+// path PATH_EDGE16 or PATH_EDGE4 (configurations with the direct-to-LDS pipeline)
+KernelRef kernels_cfg128_edge(int io, int path, int mode);
+KernelRef kernels_cfg256_edge(int io, int path, int mode);
+KernelRef kernels_cfg256w8_edge(int io, int path, int mode);
 
 }  // namespace ts

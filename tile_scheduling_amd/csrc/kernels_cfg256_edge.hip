@@ -1,0 +1,7 @@
+// Zero-filled-edge kernel instances of the 256 tile configuration (every mode
+// and type pair; B in 16-byte or 4-byte pieces).
+#include "internal.hpp"
+
+namespace ts {
+KernelRef kernels_cfg256_edge(int io, int path, int mode) { return kernel_for<Cfg256, true>(io, path, mode); }
+}  // namespace ts
