@@ -241,7 +241,8 @@ def ksweep(ts, torch, np, workloads, steps):
 
 EXTRA_SETS = (
     # (workload, schedules): the 8192 grid, every order x mode on the ragged bf16 shape,
-    # one GPU's share of an eight-way row split of the headline product, and 4096 cubed
+    # one GPU's share of an eight-way row split of the headline product, 4096 cubed, and
+    # the headline shape in bf16 and with fp32 output
     ("gemm_8192x8192x4096_f16", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped8") for r in ("", "+remap")
                                  for m in ("tiled", "persistent", "crosstile")]),
     ("gemm_5000x12290x1000_bf16_f32", [f"{o}{r}/{m}" for o in ("rowmajor", "grouped4", "grouped8", "grouped16")
@@ -250,6 +251,8 @@ EXTRA_SETS = (
                                           for m in ("tiled", "persistent", "crosstile")]),
     ("gemm_4096x4096x4096_f16", [f"{o}/{m}" for o in ("rowmajor", "grouped8+remap") for m in ("tiled", "persistent")]
      + ["grouped8+remap/crosstile", "grouped8+remap/tiled/128x128x64", "grouped8+remap/persistent/128x128x64"]),
+    ("gemm_16384x16384x4096_bf16", ["grouped8+remap/persistent", "grouped8+remap/crosstile"]),
+    ("gemm_16384x16384x4096_f16_f32", ["grouped8+remap/persistent", "grouped8+remap/crosstile"]),
 )
 
 

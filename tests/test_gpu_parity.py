@@ -249,6 +249,11 @@ def test_m_share_2048x16384x4096_sampled():
                                 for m in ("tiled", "persistent", "crosstile")])
 
 
+@pytest.mark.parametrize("w", [workloads.SQ_16384_BF16, workloads.SQ_16384_F32OUT], ids=lambda w: w.name)
+def test_headline_shape_other_types_sampled(w):
+    _large(w, [ts.Schedule(order="grouped", group_m=8, mode=m, xcd_remap=True) for m in ("persistent", "crosstile")])
+
+
 def test_4096_cubed_sampled():
     _large(workloads.SQ_4096, [ts.Schedule(order=o, group_m=8, mode=m, xcd_remap=r, tile=t)
                                for (o, r) in (("row_major", False), ("grouped", True))

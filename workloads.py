@@ -85,7 +85,11 @@ SHARE_M8 = Workload("gemm_2048x16384x4096_f16_mshare8", 2048, 16384, 4096, "f16"
 # The 4096-cubed product the grouped-ordering page also measures.
 SQ_4096 = Workload("gemm_4096x4096x4096_f16", 4096, 4096, 4096, "f16", "f16", "uniform", 1006)
 
-ALL = (SQUARE_256, SQ_8192, SQ_16384) + K_SWEEP + (RAGGED_BF16, SHARE_M8, SQ_4096)
+# The headline shape with bf16 inputs and output, and with fp16 inputs and fp32 output.
+SQ_16384_BF16 = Workload("gemm_16384x16384x4096_bf16", 16384, 16384, 4096, "bf16", "bf16", "uniform", 1007)
+SQ_16384_F32OUT = Workload("gemm_16384x16384x4096_f16_f32", 16384, 16384, 4096, "f16", "f32", "uniform", 1008)
+
+ALL = (SQUARE_256, SQ_8192, SQ_16384) + K_SWEEP + (RAGGED_BF16, SHARE_M8, SQ_4096, SQ_16384_BF16, SQ_16384_F32OUT)
 
 
 def inputs(w: Workload):
