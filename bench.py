@@ -299,8 +299,10 @@ def extras(ts, torch, np, workloads, a, b, c, w, sched, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the shader clock settles over the first few dozen launches (the board's power
+    # management); the defaults time 100 launches after 50 untimed ones
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_16384x16384x4096_f16")
     ap.add_argument("--schedule", default=DEFAULT_SCHEDULE)
     ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
