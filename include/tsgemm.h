@@ -76,7 +76,8 @@ enum {
     TS_TILE_AUTO = 0,          /* library chooses from the shape */
     TS_TILE_64x64x32 = 1,
     TS_TILE_128x128x64 = 2,
-    TS_TILE_256x256x64 = 3,    /* 4 waves of 128x128 (one per SIMD)  */
+    TS_TILE_256x256x64 = 3,    /* 4 waves of 128x128 (one per SIMD); tiled and persistent
+                                  modes only (TS_MODE_CROSSTILE: TS_ERR_UNSUPPORTED) */
     TS_TILE_256x256x64_W8 = 4  /* 8 waves of 128x64 (two per SIMD)   */
 };
 
@@ -111,6 +112,14 @@ typedef struct {
                                         /* aligned operands.                                    */
     int32_t vgprs;                      /* registers per thread reported by the runtime (-1 if none) */
     int32_t scratch_bytes;              /* private (spill) bytes per thread (-1 if none)       */
+    /* The compiler's resource report for the kernel, recorded when the library was
+       built (available without a device; -1 if the kernel is missing from it).   */
+    int32_t arch_vgprs;                 /* architectural vector registers per lane             */
+    int32_t agprs;                      /* accumulation registers (AGPRs) per lane             */
+    int32_t sgprs;                      /* scalar registers per wave                           */
+    int32_t spilled_vgprs;              /* vector registers spilled to private memory          */
+    int32_t spilled_sgprs;              /* scalar registers spilled                            */
+    int32_t compiler_occupancy;         /* waves per SIMD the compiler computed                */
 } ts_launch_info;
 
 /*
@@ -141,7 +150,7 @@ ts_status ts_gemm(const void* A, const void* B, void* C,
                   const ts_schedule* sched, void* stream);
 
 /*
- * ts_gemm with a clock record, for measurement: the same product, launch and
+ * This library's own addition, for measurement: ts_gemm with a clock record: the same product, launch and
  * errors, and in addition thread 0 of every workgroup p writes four counters to
  * the device buffer clock_out (owned by the caller, clock_rows x 4 uint64):
  *   clock_out[4p + 0 .. 1] = shader-clock counter (s_memtime) at the start and end
@@ -164,7 +173,7 @@ ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
                           uint64_t* clock_out, int64_t clock_rows);
 
 /*
- * Measurement probe: one workgroup of 8 waves per compute unit, each wave running
+ * This library's own addition, a measurement probe: one workgroup of 8 waves per compute unit, each wave running
  * `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16 with no memory traffic,
  * enqueued on `stream`.  Times the matrix cores' sustained rate on this device
  * when the caller brackets it with events: *flops (host pointer) receives the
@@ -177,7 +186,8 @@ ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
 ts_status ts_mfma_loop_probe(int32_t iters, float* sink, int64_t sink_elems, double* flops, void* stream);
 
 /*
- * Writes the work sequence of every workgroup, computed on the GPU by the same
+ * This library's own addition (the pages print no such trace): writes the work
+ * sequence of every workgroup, computed on the GPU by the same
  * device functions the GEMM kernels use, to the device buffer `out` of
  * out_rows x 5 int32: row (p * max_items + it) = (p, it, tile_m, tile_n, k_step)
  * for the it-th (tile, K-step) item workgroup p processes, where max_items =
@@ -189,7 +199,7 @@ ts_status ts_schedule_trace(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, i
                             const ts_schedule* sched, int32_t* out, int64_t out_rows, void* stream);
 
 /*
- * Host-side twin of ts_schedule_trace: the same schedule functions run on the
+ * This library's own addition: host-side twin of ts_schedule_trace: the same schedule functions run on the
  * CPU into the host buffer `out`.  `cu_count` and `programs_per_cu` stand in for
  * the device when sched->num_programs == 0 in a persistent mode.  No HIP call.
  */
@@ -199,14 +209,28 @@ ts_status ts_schedule_trace_host(int64_t M, int64_t N, int64_t K, int32_t ab_dty
 
 /*
  * Fills `out` with the launch ts_gemm would make for these arguments (tile
- * shape, tile counts, grid, occupancy, registers).  Needs a device only when the
- * grid depends on it (persistent mode with num_programs == 0) or for the
- * occupancy and register fields, which are 0 / -1 without one.
+ * shape, tile counts, grid, occupancy, registers).
+ *
+ * The persistent grid follows the grid code of the naive persistent matmul in
+ * "(1/n) Triton matmul ... persistent kernel" (num_programs = min(SMs x
+ * programs_per_sm, num_tiles)), with CUs for SMs and, for programs_per_sm, the
+ * workgroups one CU holds for the chosen kernel.  That page's section on
+ * computing the block limit by hand derives programs_per_sm from the compiled
+ * kernel's registers, spills and shared memory per block; here the HIP runtime's
+ * occupancy calculation does it (programs_per_cu), and the kernel's resource use
+ * is reported beside it: the runtime's register and private-memory figures
+ * (vgprs, scratch_bytes, lds_bytes; device needed) and the compiler's own report
+ * (arch_vgprs, agprs, sgprs, spills, compiler_occupancy; recorded at build time).
+ *
+ * Needs a device only when the grid depends on it (persistent mode with
+ * num_programs == 0) or for the runtime's occupancy and register fields, which
+ * are 0 / -1 without one.  Errors: as ts_gemm's argument checks.
  */
 ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
                    const ts_schedule* sched, ts_launch_info* out);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code.  This library's own addition
+   (the pages define no error reporting). */
 const char* ts_status_string(ts_status status);
 
 #ifdef __cplusplus

@@ -7,16 +7,20 @@ naive tiled matmul listing) replaced by fp64 so that the oracle is exact up to
 fp64 summation.  The heavy loops are in ``ref_gemm.c``; ``gemm_loop`` is a
 second, pure-Python implementation for tiny shapes.
 
-Parity pins (tests/test_oracle_gemm.py): the 4x4 worked example of section 5.1,
+Parity pins (tests/test_oracle_gemm.py): a 4x4 product with 2x2 output tiles, the
+shape of the worked example of section 5.1, against a hand expansion
+(tests/golden/gemm_4x4_int.txt; the page's own matrix values did not survive),
 identity and permutation B, rank-1 inputs, small-integer inputs against
 numpy.matmul, zeros and K = 0, brute force against ``gemm_loop``, and the
 decoders against numpy/torch conversions.
 
 Acceptance (``accept``): |C_gpu - C*| <= 2.5e-4 * S + 1e-6 elementwise, where S
 = sum_k |a_ik b_kj|; 2.5e-4 covers the worst-case fp32 summation error
-K * 2^-24 for K <= 4096.  A 16-bit output adds one unit in the last place of
-|C*| in the output format, which bounds the round-to-nearest-even conversion of
-the fp32 accumulator.
+K * 2^-24 for K <= 4096.  A 16-bit output adds the error of one round-to-
+nearest-even conversion of the fp32 accumulator x to the output type: half a
+unit in the last place at |x|.  |x| is at most |C*| + e with e = 2.5e-4 * S +
+1e-6, so the added term is ulp_out(|C*| + e) / 2 (the ulp is taken at the larger
+magnitude so that an accumulator just above a power of two is covered).
 """
 from __future__ import annotations
 
@@ -163,7 +167,8 @@ def ulp(x: np.ndarray, c_dtype: str) -> np.ndarray:
 
 
 def bound(C_ref: np.ndarray, S: np.ndarray, c_dtype: str) -> np.ndarray:
-    return REL * S + ABS + ulp(C_ref, c_dtype)
+    e = REL * S + ABS
+    return e + 0.5 * ulp(np.abs(C_ref) + e, c_dtype)
 
 
 def accept(C_gpu: np.ndarray, C_ref: np.ndarray, S: np.ndarray, c_dtype: str):

@@ -1,23 +1,36 @@
-"""Tile-order schedules as plain integer functions -- TEST INFRASTRUCTURE ONLY.
+"""Tile-order schedules as plain enumerations -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+module.  The GPU library computes every map below in closed form, with integer
+division; this module builds each one instead by walking the tile grid in the
+order the pages describe in words, and looks the answer up in the resulting
+table.  The two forms share nothing, so a slip in either shows up as a
+mismatch between the GPU trace and these tables.
 
 Sources (cited by page title and section):
   * row-major order -- "(1/n) Triton matmul ... persistent kernel", naive tiled
-    matmul listing: tile_m = tile_id // num_n_tiles, tile_n = tile_id % num_n_tiles.
+    matmul listing: tile ids run along a row of output tiles, then move to the
+    next row.
   * grouped order ("CTA swizzle") -- "(2/n) Triton matmul ... grouped ordering
-    (CTA swizzle)", section "Implementation" (the three SWIZZLE steps): groups
-    of GROUP_SIZE_M tile rows, the last group possibly shorter, and inside a
-    group the M coordinate advances first.
+    (CTA swizzle)", section "Implementation" and the prose around it: the tile
+    rows are cut into bands of GROUP_SIZE_M rows (the last band holds whatever
+    rows remain); ids fill one band completely before the next band starts,
+    and inside a band they run down a tile column (M first), then move one
+    column to the right.
   * persistent grid -- "(1/n) ...", naive persistent listing and its grid code:
     num_programs = min(CUs * programs_per_cu, num_tiles); program p takes tile
     ids p, p + P, p + 2P, ... below num_tiles.
   * flattened cross-tile loop -- "(3/n) ... cross tile pipelining", the merged
-    loop: outer_iters = cdiv(num_tiles - start, P), total = outer_iters *
-    max(K_steps, 1), tile set-up at k == 0, store at k == K_steps - 1, then k
-    wraps to 0.
-  * XCD remap -- not on the pages.  A bijection on [0, n) that sends the ids a
-    GPU with X chiplets (XCDs) deals round-robin to chiplet x (w = x, x+X, ...)
-    to one contiguous run of logical ids: w -> (w % X) * q + min(w % X, r) + w // X,
-    q = n // X, r = n % X.
+    loop.  Merging the tile loop and the K loop into one loop changes the
+    control structure, not the sequence of (tile, K step) items: the merged loop
+    visits exactly the concatenation of each tile's K steps, in the program's
+    tile order.  The page sizes that loop as total = cdiv(num_tiles - start, P)
+    * max(K_steps, 1) iterations; ``program_items`` checks its list against
+    that count.
+  * XCD remap -- not on the pages.  A GPU with X chiplets (XCDs) deals the
+    workgroups of a launch round-robin: workgroup w runs on chiplet w mod X.  The
+    remap gives chiplet 0's workgroups the first run of logical ids, chiplet 1's
+    the next run, and so on, each run in increasing w.
 
 Parity pins: tests/test_oracle_schedule.py (bijection onto the tile grid,
 G = 1 equals row-major, G >= num_m_tiles equals column-major, hand-worked
@@ -27,6 +40,7 @@ the program/tile counts the persistent page prints).
 from __future__ import annotations
 
 import dataclasses
+import functools
 
 import numpy as np
 
@@ -41,25 +55,57 @@ def cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
+@functools.lru_cache(maxsize=64)
+def row_major_table(nm: int, nn: int):
+    """Tile id -> (tile_m, tile_n): walk each tile row left to right, rows top to bottom."""
+    table = []
+    for tm in range(nm):
+        for tn in range(nn):
+            table.append((tm, tn))
+    return tuple(table)
+
+
+@functools.lru_cache(maxsize=256)
+def grouped_table(nm: int, nn: int, G: int):
+    """Tile id -> (tile_m, tile_n) of the grouped order: bands of G tile rows
+    (the last band shorter if G does not divide nm); a band is filled column by
+    column, each column top to bottom, before the next band starts."""
+    if G < 1:
+        raise ValueError("GROUP_SIZE_M must be >= 1")
+    table = []
+    band_top = 0
+    while band_top < nm:
+        band_rows = range(band_top, min(band_top + G, nm))
+        for tn in range(nn):
+            for tm in band_rows:
+                table.append((tm, tn))
+        band_top += G
+    return tuple(table)
+
+
 def row_major(t: int, nm: int, nn: int):
-    return t // nn, t % nn
+    return row_major_table(nm, nn)[t]
 
 
 def grouped(t: int, nm: int, nn: int, G: int):
-    if G < 1:
-        raise ValueError("GROUP_SIZE_M must be >= 1")
-    num_tiles_in_group = G * nn
-    group_id = t // num_tiles_in_group
-    tile_id_in_group = t % num_tiles_in_group
-    first_tile_m = group_id * G
-    group_size_m = min(G, nm - first_tile_m)
-    return first_tile_m + tile_id_in_group % group_size_m, tile_id_in_group // group_size_m
+    return grouped_table(nm, nn, G)[t]
+
+
+@functools.lru_cache(maxsize=256)
+def xcd_remap_table(n: int, X: int = 8):
+    """Launched workgroup w -> logical id: chiplet x's workgroups x, x+X, ...
+    take one contiguous run of ids, the runs in chiplet order."""
+    table = [None] * n
+    nxt = 0
+    for x in range(X):
+        for w in range(x, n, X):
+            table[w] = nxt
+            nxt += 1
+    return tuple(table)
 
 
 def xcd_remap(w: int, n: int, X: int = 8) -> int:
-    q, r = n // X, n % X
-    x = w % X
-    return x * q + min(x, r) + w // X
+    return xcd_remap_table(n, X)[w]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -89,34 +135,30 @@ def grid_size(num_tiles: int, s: Schedule) -> int:
     return min(s.num_programs, num_tiles)
 
 
-def program_items(p: int, nm: int, nn: int, ks: int, s: Schedule):
-    """The (tile_m, tile_n, k_step) items program p works through, in order."""
-    num_tiles = nm * nn
+def program_tiles(p: int, num_tiles: int, s: Schedule):
+    """Logical tile ids program p computes, in order."""
     P = grid_size(num_tiles, s)
     start = xcd_remap(p, P, s.xcds) if s.xcd_remap else p
-    ksp = max(ks, 1)
     if s.mode == TILED:
-        tiles = [start]
-    else:
-        tiles = list(range(start, num_tiles, P))
+        return [start]
+    return list(range(start, num_tiles, P))
+
+
+def program_items(p: int, nm: int, nn: int, ks: int, s: Schedule):
+    """The (tile_m, tile_n, k_step) items program p works through, in order.
+
+    Every tile keeps at least one K step (K = 0 still writes its tile)."""
+    num_tiles = nm * nn
+    ksp = max(ks, 1)
     items = []
+    for t in program_tiles(p, num_tiles, s):
+        tm, tn = tile_coords(t, nm, nn, s)
+        items.extend((tm, tn, k) for k in range(ksp))
     if s.mode == CROSSTILE:
-        # one merged loop: iteration i -> tile (start + (i // ksp) * P), k = i % ksp
-        total = cdiv(num_tiles - start, P) * ksp
-        k = 0
-        tile = start
-        for _ in range(total):
-            items.append(tile_coords(tile, nm, nn, s) + (k,))
-            if k == ksp - 1:
-                k = 0
-                tile += P
-            else:
-                k += 1
-    else:
-        for t in tiles:
-            tm, tn = tile_coords(t, nm, nn, s)
-            for k in range(ksp):
-                items.append((tm, tn, k))
+        # the merged loop's iteration count on the cross-tile page
+        P = grid_size(num_tiles, s)
+        start = xcd_remap(p, P, s.xcds) if s.xcd_remap else p
+        assert len(items) == cdiv(num_tiles - start, P) * ksp
     return items
 
 

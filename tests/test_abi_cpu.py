@@ -107,6 +107,34 @@ def test_query_tile_grid_and_masking():
     assert q["k_steps"] == 0 and q["masked"] == 1  # K = 0 still writes C (zeros)
 
 
+def test_four_wave_256_tile_has_no_crosstile_kernel():
+    s = ts.Schedule(mode="crosstile", num_programs=8, tile="256x256x64")
+    with pytest.raises(ts.TsError) as e:
+        ts.query(1024, 1024, 512, s)
+    assert e.value.status == ts.TS_ERR_UNSUPPORTED
+    assert ts.gemm_raw(FAKE, FAKE, FAKE, 1024, 1024, 512, schedule=s) == ts.TS_ERR_UNSUPPORTED
+    for mode in ("tiled", "persistent"):
+        ts.query(1024, 1024, 512, ts.Schedule(mode=mode, num_programs=8, tile="256x256x64"))
+
+
+@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("M,N,K", [(16384, 16384, 4096), (5000, 12290, 1000), (333, 290, 150)])
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
+    if tile == "256x256x64" and mode == "crosstile":
+        return
+    q = ts.query(M, N, K, ts.Schedule(mode=mode, num_programs=8, tile=tile))
+    # recorded at build time for every kernel instance: no device needed
+    assert q["arch_vgprs"] > 0 and q["agprs"] >= 0 and q["sgprs"] > 0, q
+    assert q["arch_vgprs"] + q["agprs"] <= 512
+    assert q["spilled_vgprs"] >= 0 and q["spilled_sgprs"] >= 0
+    assert q["compiler_occupancy"] >= 1
+    threads = q["threads"]
+    # one workgroup's waves must fit one CU's register file (4 SIMDs x 512 registers per lane)
+    waves_per_simd = -(-threads // 64 // 4)
+    assert waves_per_simd * (q["arch_vgprs"] + q["agprs"]) <= 512
+
+
 # ---- host-side schedule (the same functions the kernels run) vs the oracle ----------
 
 def _oracle_sched(s: ts.Schedule, grid_programs):
@@ -120,8 +148,8 @@ CASES = [
     (256, 256, 256, "64x64x32"),
     (300, 520, 200, "64x64x32"),
     (1000, 700, 96, "128x128x64"),
-    (5000, 12290, 1000, "256x256x64"),
-    (2048, 3072, 0, "256x256x64"),
+    (5000, 12290, 1000, "256x256x64w8"),
+    (2048, 3072, 0, "256x256x64w8"),
     (64, 64, 33, "64x64x32"),
 ]
 
@@ -133,7 +161,7 @@ CASES = [
 def test_host_trace_equals_oracle(M, N, K, tile, order, G, mode, P, remap):
     s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
     got = ts.schedule_trace_host(M, N, K, s)
-    bm, bn, bk = (int(v) for v in tile.split("x"))
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
     ref = osch.trace(M, N, K, bm, bn, bk, _oracle_sched(s, P))
     assert got.shape == ref.shape
     assert np.array_equal(got, ref)

@@ -14,7 +14,7 @@ import torch
 
 import workloads
 from oracle import gemm as og
-from tests.gpu_helpers import TORCH_OUT, round_to, sample_rows_cols, say, to_device, to_f64
+from tests.gpu_helpers import TORCH_OUT, round_to, sample_rows_cols, say, tile_sample, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,8 @@ def schedules(tile, P=256):
     out = []
     for (order, G), mode, remap in itertools.product([("row_major", 8), ("grouped", 8), ("grouped", 3)],
                                                       ["tiled", "persistent", "crosstile"], [False, True]):
+        if tile == "256x256x64" and mode == "crosstile":
+            continue   # no cross-tile kernel for that tile
         out.append(ts.Schedule(order=order, group_m=G, mode=mode, num_programs=0 if mode == "tiled" else P,
                                xcd_remap=remap, tile=tile))
     return out
@@ -64,7 +66,8 @@ def test_integer_inputs_bit_exact(tile, ab, c_dtype):
     A, B = workloads.pair(M, N, K, ab, "int", 500)
     C, _ = og.gemm(A, B, ab, threads=4)
     expect = round_to(C, c_dtype)
-    for sched in (ts.Schedule(tile=tile), ts.Schedule(order="grouped", group_m=3, mode="crosstile",
+    second = "persistent" if tile == "256x256x64" else "crosstile"   # no cross-tile kernel for that tile
+    for sched in (ts.Schedule(tile=tile), ts.Schedule(order="grouped", group_m=3, mode=second,
                                                       num_programs=5, tile=tile)):
         got = to_f64(run(A, B, ab, c_dtype, sched, M, N, K))
         bad = np.argwhere(got != expect)
@@ -80,6 +83,8 @@ def test_aligned_integer_inputs_bit_exact(tile):
     C, _ = og.gemm(A, B, "f16")
     assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == 0
     for mode in ("tiled", "persistent", "crosstile"):
+        if tile == "256x256x64" and mode == "crosstile":
+            continue   # no cross-tile kernel for that tile
         got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode=mode, num_programs=4, tile=tile), M, N, K))
         assert np.array_equal(got, C), mode
 
@@ -182,7 +187,8 @@ def test_ragged_bf16_5000x12290x1000_full_size():
     for sched in [ts.Schedule(tile="256x256x64"),
                   ts.Schedule(order="grouped", group_m=8, tile="256x256x64"),
                   ts.Schedule(order="grouped", group_m=8, mode="persistent", tile="256x256x64"),
-                  ts.Schedule(order="grouped", group_m=8, mode="crosstile", xcd_remap=True, tile="256x256x64"),
+                  ts.Schedule(order="grouped", group_m=8, mode="persistent", num_programs=3, xcd_remap=True,
+                              tile="256x256x64"),
                   ts.Schedule(order="grouped", group_m=16, mode="persistent", xcd_remap=True, tile="256x256x64"),
                   # 8 waves: same per-element accumulation order, so bit-identical too
                   ts.Schedule(order="grouped", group_m=8, mode="tiled", xcd_remap=True, tile="256x256x64w8"),
@@ -206,7 +212,12 @@ def test_ragged_bf16_5000x12290x1000_full_size():
 
 # ---- the large square workloads, in the launch configurations the benchmark times ----
 
-def _large(w, scheds):
+def _large(w, scheds, BM=256, BN=256):
+    """Every schedule bit-identical to the first; then, on the first schedule's C,
+    whole output tiles (every edge class, the first and last tile of each band of
+    the grouped orders and of each XCD's run, 64 random tiles) and whole rows and
+    columns (both edges of every tile-boundary class and random ones) against
+    the oracle."""
     A, B = workloads.inputs(w)
     a, b = to_device(A, w.ab_dtype), to_device(B, w.ab_dtype)
     base = None
@@ -221,13 +232,24 @@ def _large(w, scheds):
             assert torch.equal(c, base), s.label()
             del c
     rng = np.random.default_rng(11)
-    rows, cols = sample_rows_cols(w.M, w.N, 256, 256, rng, extra=3)
-    for r in rows[:10]:
-        C, S = og.gemm(A, B, w.ab_dtype, rows=(int(r), int(r) + 1))
-        assert_accept(to_f64(base[r:r + 1]), C, S, w.c_dtype, f"row {r}")
-    for cidx in cols[:6]:
-        C, S = og.gemm(A, B, w.ab_dtype, cols=(int(cidx), int(cidx) + 1), threads=8)
-        assert_accept(to_f64(base[:, cidx:cidx + 1]), C, S, w.c_dtype, f"col {cidx}")
+    tiles = tile_sample(w.M, w.N, BM, BN, rng)
+    assert len(tiles) >= 64
+    threads = max(1, min(16, og.max_threads()))
+    worst = 0.0
+    for tm, tn in tiles:
+        r0, r1 = tm * BM, min(w.M, (tm + 1) * BM)
+        c0, c1 = tn * BN, min(w.N, (tn + 1) * BN)
+        C, S = og.gemm(A, B, w.ab_dtype, rows=(r0, r1), cols=(c0, c1), threads=threads)
+        worst = max(worst, assert_accept(to_f64(base[r0:r1, c0:c1]), C, S, w.c_dtype, f"tile ({tm}, {tn})"))
+    rows, cols = sample_rows_cols(w.M, w.N, BM, BN, rng, extra=3)
+    for r in rows:
+        C, S = og.gemm(A, B, w.ab_dtype, rows=(int(r), int(r) + 1), threads=threads)
+        worst = max(worst, assert_accept(to_f64(base[r:r + 1]), C, S, w.c_dtype, f"row {r}"))
+    for cidx in cols:
+        C, S = og.gemm(A, B, w.ab_dtype, cols=(int(cidx), int(cidx) + 1), threads=threads)
+        worst = max(worst, assert_accept(to_f64(base[:, cidx:cidx + 1]), C, S, w.c_dtype, f"col {cidx}"))
+    say(f"{w.name}: {len(tiles)} tiles, {len(rows)} rows, {len(cols)} columns checked; "
+        f"worst |err|/bound {worst:.3g}")
 
 
 def test_8192x8192x4096_sampled():
@@ -260,7 +282,7 @@ def test_4096_cubed_sampled():
                                for m in ("tiled", "persistent", "crosstile") for t in ("auto",)])
 
 
-@pytest.mark.parametrize("w", workloads.K_SWEEP[:4], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", workloads.K_SWEEP, ids=lambda w: w.name)
 def test_k_sweep_sampled(w):
     _large(w, [ts.Schedule(order="grouped", group_m=8, mode="persistent", xcd_remap=True),
                ts.Schedule(order="grouped", group_m=8, mode="crosstile", xcd_remap=True)])
@@ -281,6 +303,8 @@ def test_empty_outputs_are_untouched():
 @pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
 @pytest.mark.parametrize("tile", TILES)
 def test_k_zero_writes_zeros(mode, tile):
+    if tile == "256x256x64" and mode == "crosstile":
+        pytest.skip("no cross-tile kernel for the 4-wave 256 x 256 x 64 tile (rejected on the host)")
     a = torch.zeros((300, 0), dtype=torch.float16, device="cuda")
     b = torch.zeros((0, 270), dtype=torch.float16, device="cuda")
     c = torch.full((300, 270), float("nan"), dtype=torch.float16, device="cuda")
@@ -295,7 +319,8 @@ def test_tiny_shapes(M, N, K):
     A, B = workloads.pair(M, N, K, "f16", "int", 70)
     C, _ = og.gemm(A, B, "f16")
     for tile in TILES:
-        got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode="crosstile", num_programs=2, tile=tile), M, N, K))
+        mode = "persistent" if tile == "256x256x64" else "crosstile"
+        got = to_f64(run(A, B, "f16", "f32", ts.Schedule(mode=mode, num_programs=2, tile=tile), M, N, K))
         assert np.array_equal(got, C), tile
 
 
@@ -339,6 +364,8 @@ def test_edge_paths_padded_operands_with_canaries(tile, N):
     cbuf = torch.full((M + 4, N + 2 * pad + 2), -12345.0, device="cuda")
     c = cbuf[2:2 + M, pad:pad + N]
     for mode in ("tiled", "persistent", "crosstile"):
+        if tile == "256x256x64" and mode == "crosstile":
+            continue   # no cross-tile kernel for that tile
         say(f"edge canaries {tile} N={N} {mode}")
         ts.gemm(a, b, out=c, schedule=ts.Schedule(order="grouped", group_m=2, mode=mode, num_programs=3,
                                                   tile=tile))

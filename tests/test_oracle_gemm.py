@@ -45,6 +45,41 @@ def test_decode_bf16_all_patterns():
     assert og.decode(np.array([0x0001], np.uint16), "bf16")[0] == 2.0 ** -133
 
 
+# ---- the 4x4, 2x2-tile example against a hand expansion ------------------------------
+
+def _golden_blocks(name):
+    import os
+
+    blocks, cur = {}, None
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line[0].isalpha():
+                cur = blocks.setdefault(line, [])
+            else:
+                cur.append([float(v) for v in line.split()])
+    return {k: np.array(v, dtype=np.float64) for k, v in blocks.items()}
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_4x4_worked_shape_against_hand_expansion(dtype):
+    # "Week-4 notes: Roofline and Tiling", section 5.1: 4x4 output, 2x2 tiles, K
+    # slices of 2.  Values and expected sums are in tests/golden/gemm_4x4_int.txt.
+    g = _golden_blocks("gemm_4x4_int.txt")
+    C, S = og.gemm(_bits(g["A"], dtype), _bits(g["B"], dtype), dtype)
+    assert np.array_equal(C, g["C"])
+    assert np.array_equal(S, g["S"])
+    # tile (0, 0) as the sum of its two K-slice products, each expanded by hand
+    s0, s1 = og.gemm(_bits(g["A"][0:2, 0:2], dtype), _bits(g["B"][0:2, 0:2], dtype), dtype)[0], \
+        og.gemm(_bits(g["A"][0:2, 2:4], dtype), _bits(g["B"][2:4, 0:2], dtype), dtype)[0]
+    assert np.array_equal(s0, g["slice0"]) and np.array_equal(s1, g["slice1"])
+    assert np.array_equal(s0 + s1, C[0:2, 0:2])
+    # 2MNK = 128 floating point operations: 64 products, each followed by one add
+    assert 2 * C.size * g["A"].shape[1] == 128
+
+
 # ---- closed forms -------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -177,6 +212,16 @@ def test_accept_detects_planted_errors():
     # rounding C to fp16 (RNE) stays inside the widened bound
     ok, _, _ = og.accept(C.astype(np.float16).astype(np.float64), C, S, "f16")
     assert ok
+    # rounding the wrong way (one whole ulp off) is caught where S is small next to |C|
+    ones = np.ones((4, 4))
+    Sx = np.full((4, 4), 1.0)
+    Cx = np.full((4, 4), 1.0 + 3 * 2.0 ** -11)      # halfway point between two fp16 values + 2^-11
+    up = np.float64(np.float16(1.0 + 4 * 2.0 ** -11))
+    down = np.float64(np.float16(1.0 + 2 * 2.0 ** -11))
+    assert og.accept(np.full((4, 4), up), Cx, Sx * 0, "f16")[0]
+    assert og.accept(np.full((4, 4), down), Cx, Sx * 0, "f16")[0]
+    assert not og.accept(np.full((4, 4), up + 2.0 ** -10), Cx, Sx * 0, "f16")[0]
+    assert not og.accept(ones * (down - 2.0 ** -10), Cx, Sx * 0, "f16")[0]
     # a dropped term is caught
     a, b = og.decode(A, dtype), og.decode(B, dtype)
     wrong = C - a[:, 5:6] * b[5:6, :]

@@ -44,7 +44,9 @@ class LaunchInfo(ctypes.Structure):
     _fields_ = [("block_m", _i32), ("block_n", _i32), ("block_k", _i32), ("threads", _i32),
                 ("num_m_tiles", _i64), ("num_n_tiles", _i64), ("k_steps", _i64), ("num_tiles", _i64),
                 ("grid", _i64), ("programs_per_cu", _i32), ("cu_count", _i32), ("xcds", _i32),
-                ("lds_bytes", _i32), ("masked", _i32), ("vgprs", _i32), ("scratch_bytes", _i32)]
+                ("lds_bytes", _i32), ("masked", _i32), ("vgprs", _i32), ("scratch_bytes", _i32),
+                ("arch_vgprs", _i32), ("agprs", _i32), ("sgprs", _i32), ("spilled_vgprs", _i32),
+                ("spilled_sgprs", _i32), ("compiler_occupancy", _i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -3,13 +3,16 @@
 // schedule trace.  See include/tsgemm.h for the contract of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
 #include <limits.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
 #include "../../include/tsgemm.h"
 #include "internal.hpp"
+#include "resource_table.hpp"
 
 namespace ts {
 
@@ -110,6 +113,21 @@ int choose_path(const Plan& p, int64_t N, int64_t K, uintptr_t a, uintptr_t b, i
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The compiler's resource report of a kernel, found through the symbol name of its
+// launch handle (the handle's symbol carries the kernel's mangled name).
+const KernelResources* resources_of(const void* fn) {
+    Dl_info info;
+    if (!fn || !dladdr(fn, &info) || !info.dli_sname) return nullptr;
+    int lo = 0, hi = kNumKernelResources - 1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) / 2;
+        const int c = strcmp(kKernelResources[mid].name, info.dli_sname);
+        if (c == 0) return &kKernelResources[mid];
+        if (c < 0) lo = mid + 1; else hi = mid - 1;
+    }
+    return nullptr;
+}
+
 // Shape-only checks and choices, shared by every entry point.  Row strides and
 // base addresses (which only ts_gemm has) refine the vector flags later.
 ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, const ts_schedule* sp,
@@ -143,6 +161,8 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
         else if (cdiv64(M, 128) * cdiv64(N, 128) >= 128) cfg = CFG_128;
         else cfg = CFG_64;
     }
+    // the 4-wave 256 x 256 x 64 tile has no cross-tile kernel (see has_flat_kernel)
+    if (cfg == CFG_256 && s.mode == TS_MODE_CROSSTILE) return TS_ERR_UNSUPPORTED;
     p->cfg = cfg;
     cfg_dims(cfg, &p->bm, &p->bn, &p->bk);
     const int64_t nm = cdiv64(M, p->bm), nn = cdiv64(N, p->bn), ks = cdiv64(K, p->bk);
@@ -343,6 +363,13 @@ extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
     out->masked = p.path;
     out->vgprs = -1;
     out->scratch_bytes = -1;
+    const KernelResources* kr = resources_of(k.fn);
+    out->arch_vgprs = kr ? kr->vgprs : -1;
+    out->agprs = kr ? kr->agprs : -1;
+    out->sgprs = kr ? kr->sgprs : -1;
+    out->spilled_vgprs = kr ? kr->vgpr_spill : -1;
+    out->spilled_sgprs = kr ? kr->sgpr_spill : -1;
+    out->compiler_occupancy = kr ? kr->occupancy : -1;
     if (have_dev) {
         hipFuncAttributes fa;
         if (hipFuncGetAttributes(&fa, k.fn) == hipSuccess) {

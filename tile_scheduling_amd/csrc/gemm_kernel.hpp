@@ -1161,7 +1161,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     FlatPos ld = p1;                   // next item whose slices are loaded (DA = DB ahead)
     static_assert(E::DA == E::DB, "one load cursor");
     if (E::DA == 2) ld.template advance<Cfg>(g.s, w);
-    // cursors past the program's last item produce coordinates that are never read
+    // cursors past the program's last item get tile (0, 0) from tile_coords; nothing
+    // is loaded (record count 0) or stored for them
 
     int it = 0;
     bool stored = false;               // the item before ended a tile (its stores are in flight)

@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gemm_kernel.hpp"
 
 namespace ts {
@@ -24,12 +26,22 @@ struct KernelRef {
     int lds_bytes;   // static LDS of the instance
 };
 
+// Whether a configuration has a cross-tile (flattened loop) kernel.  The 4-wave
+// 256 x 256 x 64 tile has none: its 256 accumulators per lane do not survive the
+// flattened loop's branch merges without about a thousand spilled registers.
+template <class Cfg>
+constexpr bool has_flat_kernel() { return !std::is_same<Cfg, Cfg256>::value; }
+
 template <class Cfg, class TI, class TO, int PATH>
 const void* kernel_by_mode(int mode) {
     switch (mode) {
         case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_TILED>);
         case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_PERSISTENT>);
-        default: return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);
+        default:
+            if constexpr (has_flat_kernel<Cfg>())
+                return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);
+            else
+                return nullptr;
     }
 }
 

@@ -60,8 +60,13 @@ TS_HD int xcd_remap(int w, int n, int X) {
     return x * q + min_i(x, r) + w / X;
 }
 
+// Ids at or past num_tiles (the cursors of the flattened loop run ahead of the
+// last tile) map to (0, 0), so that no division by a band of zero rows occurs;
+// nothing is loaded or stored for them.
 TS_HD void tile_coords(const SchedArgs& s, int t, int& tm, int& tn) {
-    if (s.order == ORDER_GROUPED) {
+    if (t >= s.num_tiles) {
+        tm = tn = 0;
+    } else if (s.order == ORDER_GROUPED) {
         const int in_group = s.group_m * s.nn;            // tiles per full group
         const int gid = t / in_group;
         const int tig = t - gid * in_group;               // id inside the group
