@@ -68,7 +68,17 @@ enum {
     /* as PERSISTENT, but the tile loop and the K loop are one flattened loop, so
        the next tile's first K slices are fetched while the current tile is being
        stored ("(3/n) ... cross tile pipelining", merged loop) */
-    TS_MODE_CROSSTILE = 2
+    TS_MODE_CROSSTILE = 2,
+    /* stream-K, the follow-on the persistent page names for its tail (the split is
+       this library's design): the first num_tiles - (num_tiles mod P) tiles run as
+       in PERSISTENT; the (tile, K step) items of the remaining tiles are dealt to all
+       P programs as contiguous ranges of equal length (+-1), program p taking range
+       P-1-p.  The program holding K step 0 of a split tile adds the other ranges'
+       fp32 partial tiles, in range order, and stores it; the result is identical
+       from run to run but not bit-identical to the other modes (a different
+       summation order along K).  Needs a workspace: ts_gemm_workspace, sized by
+       ts_query's workspace_bytes (0 when no tile is split). */
+    TS_MODE_STREAMK = 3
 };
 
 /* tile configurations (BLOCK_M x BLOCK_N x BLOCK_K) */
@@ -106,10 +116,13 @@ typedef struct {
     int32_t xcds;                       /* XCDs the workgroups are dealt over (8 if no device) */
     int32_t lds_bytes;                  /* LDS per workgroup                                   */
     int32_t masked;                     /* kernel path: 0 whole tiles; 1 masked register        */
-                                        /* pipeline (ragged or unaligned); 2 / 3 direct-to-LDS  */
-                                        /* pipeline with zero-filled edges, B loaded in 16- /   */
-                                        /* 4-byte pieces.  ts_query assumes dense, 16-byte      */
-                                        /* aligned operands.                                    */
+                                        /* pipeline (ragged or unaligned); 2 direct-to-LDS      */
+                                        /* pipeline with edges zero-filled by the loads' range  */
+                                        /* checks.  ts_query assumes dense, 16-byte aligned     */
+                                        /* operands.                                            */
+    int64_t workspace_bytes;            /* TS_MODE_STREAMK: workspace the launch needs (0: none) */
+    int64_t trace_items;                /* most (tile, K step) items of one workgroup: the row
+                                           stride of ts_schedule_trace's output                */
     int32_t vgprs;                      /* registers per thread reported by the runtime (-1 if none) */
     int32_t scratch_bytes;              /* private (spill) bytes per thread (-1 if none)       */
     /* The compiler's resource report for the kernel, recorded when the library was
@@ -133,13 +146,15 @@ typedef struct {
  *   Ragged M, N, K and row strides that defeat 16-byte vector access are handled
  *   by masked loads and stores (out-of-range A and B elements read as zero; C is
  *   written only inside M x N).  When K and A's row stride are multiples of 8
- *   elements with A 16-byte aligned, and B's base, row stride and N allow 16- or
- *   4-byte pieces, the edges are zero-filled by the direct-to-LDS loads themselves
+ *   elements with A 16-byte aligned, and B's base is 4-byte aligned with its row
+ *   stride and N even, the edges are zero-filled by the direct-to-LDS loads themselves
  *   (no element-wise masking).  sched == NULL means row-major tiled, auto tile.
  *   The result does not depend on the schedule: every schedule with the same tile
  *   configuration produces bit-identical C.
  *   Errors: TS_ERR_INVALID_ARG / TS_ERR_UNSUPPORTED / TS_ERR_ALIGNMENT before any
  *   HIP call; TS_ERR_NO_DEVICE if no GPU; TS_ERR_HIP if the launch fails.
+ *   A TS_MODE_STREAMK launch that splits tiles needs a workspace: call
+ *   ts_gemm_workspace (here it returns TS_ERR_INVALID_ARG).
  */
 ts_status ts_gemm(const void* A, const void* B, void* C,
                   int64_t M, int64_t N, int64_t K,
@@ -148,6 +163,30 @@ ts_status ts_gemm(const void* A, const void* B, void* C,
                   int64_t stride_cm, int64_t stride_cn,
                   int32_t ab_dtype, int32_t c_dtype,
                   const ts_schedule* sched, void* stream);
+
+/*
+ * ts_gemm with a caller-owned device workspace, for schedules that need one
+ * (TS_MODE_STREAMK; see there).  workspace_bytes must be at least ts_query's
+ * workspace_bytes for the same arguments and the workspace 256-byte aligned,
+ * else TS_ERR_INVALID_ARG; launches that need no workspace accept NULL.
+ * Layout: int32 flags[P] (P = ts_query's grid), int32 timeouts, padding to 256
+ * bytes, then P partial tiles of block_m x block_n fp32.  The header (flags and
+ * timeout counter) must be zero before the first call on a workspace; every
+ * call leaves the flags zero again.  The timeout counter counts waits for
+ * another workgroup's partial tile that gave up after about a second (possible
+ * only if other work keeps that workgroup from running; the result is then
+ * wrong); it is never reset by the library.  Calls that share a workspace must
+ * not overlap in time (use one stream, or one workspace per stream).
+ * Otherwise as ts_gemm.
+ */
+ts_status ts_gemm_workspace(const void* A, const void* B, void* C,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t stride_am, int64_t stride_ak,
+                            int64_t stride_bk, int64_t stride_bn,
+                            int64_t stride_cm, int64_t stride_cn,
+                            int32_t ab_dtype, int32_t c_dtype,
+                            const ts_schedule* sched, void* stream,
+                            void* workspace, int64_t workspace_bytes);
 
 /*
  * This library's own addition, for measurement: ts_gemm with a clock record: the same product, launch and
@@ -161,7 +200,8 @@ ts_status ts_gemm(const void* A, const void* B, void* C,
  * is the shader clock the workgroup ran at.  Used to state a kernel's MFMA
  * utilisation at the clock the board's power limit actually allowed.
  * clock_rows must be >= the launch grid (ts_query), else TS_ERR_INVALID_ARG;
- * clock_out == NULL is TS_ERR_INVALID_ARG.
+ * clock_out == NULL is TS_ERR_INVALID_ARG.  workspace / workspace_bytes: as in
+ * ts_gemm_workspace (NULL / 0 when the schedule needs none).
  */
 ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
                           int64_t M, int64_t N, int64_t K,
@@ -170,7 +210,8 @@ ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
                           int64_t stride_cm, int64_t stride_cn,
                           int32_t ab_dtype, int32_t c_dtype,
                           const ts_schedule* sched, void* stream,
-                          uint64_t* clock_out, int64_t clock_rows);
+                          uint64_t* clock_out, int64_t clock_rows,
+                          void* workspace, int64_t workspace_bytes);
 
 /*
  * This library's own addition, a measurement probe: one workgroup of 8 waves per compute unit, each wave running
@@ -191,8 +232,9 @@ ts_status ts_mfma_loop_probe(int32_t iters, float* sink, int64_t sink_elems, dou
  * device functions the GEMM kernels use, to the device buffer `out` of
  * out_rows x 5 int32: row (p * max_items + it) = (p, it, tile_m, tile_n, k_step)
  * for the it-th (tile, K-step) item workgroup p processes, where max_items =
- * cdiv(num_tiles, grid) * max(k_steps, 1); rows past a workgroup's item count are
- * filled with -1.  out_rows must be >= grid * max_items (see ts_query).
+ * ts_query's trace_items (cdiv(num_tiles, grid) * max(k_steps, 1) except in
+ * stream-K mode); rows past a workgroup's item count are filled with -1.
+ * out_rows must be >= grid * max_items.
  * Same validation and error codes as ts_gemm (no matrix pointers involved).
  */
 ts_status ts_schedule_trace(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,

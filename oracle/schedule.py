@@ -27,6 +27,14 @@ Sources (cited by page title and section):
     tile order.  The page sizes that loop as total = cdiv(num_tiles - start, P)
     * max(K_steps, 1) iterations; ``program_items`` checks its list against
     that count.
+  * stream-K -- the persistent page names it as the follow-on for the tail of
+    the persistent grid; how the tail is split is this library's own design,
+    restated here from its definition: the first num_tiles - (num_tiles mod P)
+    tiles (whole rounds of P programs) run as in the persistent mode; the K steps
+    of the remaining tiles, listed tile by tile in tile-id order and k ascending
+    inside a tile, are cut into P consecutive pieces whose lengths differ by at
+    most one, longer pieces first (numpy.array_split's rule); piece r goes to
+    program P - 1 - r, which runs it before its whole tiles.
   * XCD remap -- not on the pages.  A GPU with X chiplets (XCDs) deals the
     workgroups of a launch round-robin: workgroup w runs on chiplet w mod X.  The
     remap gives chiplet 0's workgroups the first run of logical ids, chiplet 1's
@@ -49,6 +57,7 @@ GROUPED = "grouped"
 TILED = "tiled"
 PERSISTENT = "persistent"
 CROSSTILE = "crosstile"
+STREAMK = "streamk"
 
 
 def cdiv(a: int, b: int) -> int:
@@ -126,13 +135,27 @@ def tile_coords(t: int, nm: int, nn: int, s: Schedule):
     raise ValueError(s.order)
 
 
-def grid_size(num_tiles: int, s: Schedule) -> int:
-    """Programs launched: one per tile when tiled, else min(P, num_tiles)."""
+def grid_size(num_tiles: int, s: Schedule, ks: int = 1) -> int:
+    """Programs launched: one per tile when tiled, min(P, num_tiles) when
+    persistent, and min(P, num_tiles * max(ks, 1)) for stream-K (no more programs
+    than (tile, K step) items)."""
     if s.mode == TILED:
         return num_tiles
     if s.num_programs < 1:
         raise ValueError("persistent schedules need num_programs >= 1")
+    if s.mode == STREAMK:
+        return min(s.num_programs, num_tiles * max(ks, 1))
     return min(s.num_programs, num_tiles)
+
+
+def streamk_split(num_tiles: int, ks: int, P: int):
+    """(whole tiles, pieces): the tiles run whole, and piece r of the split (tile
+    id, k) items for r = 0 .. P-1."""
+    split_tiles = num_tiles % P if ks > 0 else 0
+    whole = num_tiles - split_tiles
+    items = [(t, k) for t in range(whole, num_tiles) for k in range(ks)]
+    pieces = [[items[i] for i in idx] for idx in np.array_split(np.arange(len(items)), P)]
+    return whole, pieces
 
 
 def program_tiles(p: int, num_tiles: int, s: Schedule):
@@ -151,6 +174,16 @@ def program_items(p: int, nm: int, nn: int, ks: int, s: Schedule):
     num_tiles = nm * nn
     ksp = max(ks, 1)
     items = []
+    if s.mode == STREAMK:
+        P = grid_size(num_tiles, s, ks)
+        whole, pieces = streamk_split(num_tiles, ks, P)
+        for t, k in pieces[P - 1 - p]:
+            items.append(tile_coords(t, nm, nn, s) + (k,))
+        start = xcd_remap(p, P, s.xcds) if s.xcd_remap else p
+        for t in range(start, whole, P):
+            tm, tn = tile_coords(t, nm, nn, s)
+            items.extend((tm, tn, k) for k in range(ksp))
+        return items
     for t in program_tiles(p, num_tiles, s):
         tm, tn = tile_coords(t, nm, nn, s)
         items.extend((tm, tn, k) for k in range(ksp))
@@ -170,11 +203,15 @@ def trace(M: int, N: int, K: int, BM: int, BN: int, BK: int, s: Schedule):
     """
     nm, nn, ks = cdiv(M, BM), cdiv(N, BN), cdiv(K, BK)
     num_tiles = nm * nn
-    P = grid_size(num_tiles, s) if num_tiles else 0
+    P = grid_size(num_tiles, s, ks) if num_tiles else 0
     ksp = max(ks, 1)
-    max_items = (cdiv(num_tiles, P) if P else 0) * ksp
+    per_program = [program_items(p, nm, nn, ks, s) for p in range(P)]
+    if s.mode == STREAMK:
+        max_items = max((len(x) for x in per_program), default=0)
+    else:
+        max_items = (cdiv(num_tiles, P) if P else 0) * ksp
     out = np.full((P * max_items, 5), -1, dtype=np.int32)
     for p in range(P):
-        for it, (tm, tn, k) in enumerate(program_items(p, nm, nn, ks, s)):
+        for it, (tm, tn, k) in enumerate(per_program[p]):
             out[p * max_items + it] = (p, it, tm, tn, k)
     return out

@@ -68,7 +68,7 @@ def test_invalid_arguments_are_rejected(kw, expect):
 def test_bad_schedule_enums_are_rejected():
     s = ts._Schedule(5, 1, 0, 0, 0, 0)
     assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(s), None) == -1
-    for bad in (ts._Schedule(0, 1, 3, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9)):
+    for bad in (ts._Schedule(0, 1, 4, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9)):
         assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(bad), None) == -1
 
 
@@ -91,8 +91,8 @@ def test_query_tile_grid_and_masking():
     q = ts.query(5000, 12290, 1000, ts.Schedule(mode="persistent", num_programs=256, tile="256x256x64"),
                  ts.TS_BF16, ts.TS_F32)
     assert (q["num_m_tiles"], q["num_n_tiles"], q["k_steps"]) == (20, 49, 16)
-    assert q["grid"] == 256 and q["masked"] == 3   # edge path, B rows in 4-byte pieces
-    # kernel path: whole tiles 0, masked registers 1, zero-filled edges 2 (16-byte B) or 3 (4-byte B)
+    assert q["grid"] == 256 and q["masked"] == 2   # edge path (B rows only 4-byte aligned)
+    # kernel path: whole tiles 0, masked registers 1, zero-filled edges 2
     assert ts.query(1000, 1024, 512, ts.Schedule(tile="256x256x64"))["masked"] == 2
     assert ts.query(1000, 1025, 512, ts.Schedule(tile="256x256x64"))["masked"] == 1   # N odd
     assert ts.query(1000, 1024, 500, ts.Schedule(tile="256x256x64"))["masked"] == 1   # K not 0 mod 8
@@ -138,7 +138,8 @@ def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
 # ---- host-side schedule (the same functions the kernels run) vs the oracle ----------
 
 def _oracle_sched(s: ts.Schedule, grid_programs):
-    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE}[s.mode]
+    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE,
+            "streamk": osch.STREAMK}[s.mode]
     order = osch.GROUPED if s.order == "grouped" else osch.ROW_MAJOR
     return osch.Schedule(order=order, group_m=s.group_m, mode=mode, num_programs=grid_programs,
                          xcd_remap=s.xcd_remap)
@@ -156,7 +157,8 @@ CASES = [
 
 @pytest.mark.parametrize("M,N,K,tile", CASES)
 @pytest.mark.parametrize("order,G", [("row_major", 1), ("grouped", 3), ("grouped", 8), ("grouped", 100)])
-@pytest.mark.parametrize("mode,P", [("tiled", 0), ("persistent", 7), ("persistent", 256), ("crosstile", 256)])
+@pytest.mark.parametrize("mode,P", [("tiled", 0), ("persistent", 7), ("persistent", 256), ("crosstile", 256),
+                                    ("streamk", 7), ("streamk", 256)])
 @pytest.mark.parametrize("remap", [False, True])
 def test_host_trace_equals_oracle(M, N, K, tile, order, G, mode, P, remap):
     s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
@@ -174,3 +176,34 @@ def test_host_trace_auto_grid_uses_cus_times_occupancy():
     assert np.array_equal(got, ref)
     with pytest.raises(ts.TsError):
         ts.schedule_trace_host(8192, 8192, 4096, s)  # no device and no CU count given
+
+
+@pytest.mark.parametrize("M,N,K,tile,P", [(5000, 12290, 1000, "256x256x64w8", 256), (300, 520, 200, "64x64x32", 7),
+                                         (1000, 700, 96, "128x128x64", 512), (512, 512, 0, "128x128x64", 5),
+                                         (8192, 8192, 4096, "256x256x64w8", 256)])
+def test_streamk_workspace_size(M, N, K, tile, P):
+    q = ts.query(M, N, K, ts.Schedule(mode="streamk", num_programs=P, tile=tile))
+    T, ks, grid = q["num_tiles"], q["k_steps"], q["grid"]
+    assert grid == min(P, T * max(ks, 1))
+    split = T % grid if ks > 0 else 0
+    if split == 0:
+        assert q["workspace_bytes"] == 0
+    else:
+        header = -(-(grid + 1) * 4 // 256) * 256
+        assert q["workspace_bytes"] == header + grid * q["block_m"] * q["block_n"] * 4
+    for mode in ("tiled", "persistent", "crosstile"):
+        assert ts.query(M, N, K, ts.Schedule(mode=mode, num_programs=P, tile=tile))["workspace_bytes"] == 0
+
+
+def test_streamk_needs_its_workspace():
+    s = ts.Schedule(mode="streamk", num_programs=256, tile="256x256x64w8")
+    need = ts.query(5000, 12290, 1000, s, ts.TS_BF16, ts.TS_F32)["workspace_bytes"]
+    assert need > 0
+    args = [FAKE, FAKE, FAKE, 5000, 12290, 1000, 1000, 1, 12290, 1, 12290, 1, ts.TS_BF16, ts.TS_F32,
+            ctypes.byref(s._c()), None]
+    # without a workspace, too small, or misaligned: rejected before any HIP call
+    assert ts._lib.ts_gemm(*args) == ts.TS_ERR_INVALID_ARG
+    assert ts._lib.ts_gemm_workspace(*args, None, 0) == ts.TS_ERR_INVALID_ARG
+    assert ts._lib.ts_gemm_workspace(*args, FAKE, need - 1) == ts.TS_ERR_INVALID_ARG
+    assert ts._lib.ts_gemm_workspace(*args, FAKE + 16, need) == ts.TS_ERR_INVALID_ARG
+    assert ts._lib.ts_gemm_workspace(*args, FAKE, -1) == ts.TS_ERR_INVALID_ARG

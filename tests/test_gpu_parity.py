@@ -143,14 +143,14 @@ def test_ragged_word_aligned_rows(tile, ab, c_dtype):
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("ab,c_dtype", IO)
-@pytest.mark.parametrize("n_tail", [8, 2], ids=["edge16", "edge4"])
+@pytest.mark.parametrize("n_tail", [8, 2], ids=["b16aligned", "b4aligned"])
 def test_ragged_edge_paths(tile, ab, c_dtype, n_tail):
     # K a multiple of 8 with a partial last slice, M and N ragged: the direct-to-LDS
-    # tiles zero-fill the edges (B in 16-byte pieces when N = 0 mod 8, else 4-byte);
-    # the 64-wide tile has no such pipeline and runs masked
+    # tiles zero-fill the edges (B rows 16-byte aligned when N = 0 mod 8, else only
+    # 4-byte aligned); the 64-wide tile has no such pipeline and runs masked
     bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
     M, N, K = 2 * bm + 5, 3 * bn + n_tail, 4 * bk + 8
-    expect_path = 1 if tile == "64x64x32" else (2 if n_tail == 8 else 3)
+    expect_path = 1 if tile == "64x64x32" else 2
     assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == expect_path
     A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 620)
     C, S = og.gemm(A, B, ab, threads=4)
@@ -195,7 +195,7 @@ def test_ragged_bf16_5000x12290x1000_full_size():
                   ts.Schedule(order="grouped", group_m=8, mode="crosstile", tile="256x256x64w8")]:
         q = ts.query(w.M, w.N, w.K, sched, ts.TS_BF16, ts.TS_F32)
         # edges zero-filled by the direct-to-LDS loads, B's 4-byte aligned rows in 4-byte pieces
-        assert q["masked"] == 3 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
+        assert q["masked"] == 2 and q["num_m_tiles"] == 20  # G = 8 leaves a short last group of 4 rows
         c = run(A, B, w.ab_dtype, w.c_dtype, sched, w.M, w.N, w.K)
         if base is None:
             base = c
@@ -349,7 +349,7 @@ def test_padded_and_unaligned_operands_with_canaries(tile):
 
 
 @pytest.mark.parametrize("tile", ["128x128x64", "256x256x64", "256x256x64w8"])
-@pytest.mark.parametrize("N", [296, 290], ids=["edge16", "edge4"])
+@pytest.mark.parametrize("N", [296, 290], ids=["b16aligned", "b4aligned"])
 def test_edge_paths_padded_operands_with_canaries(tile, N):
     # padded row strides (8 elements) on the zero-filled-edge paths: the loads stop at
     # each matrix's last element, the stores stay inside C
@@ -386,7 +386,7 @@ def test_deterministic():
 
 # ---- the clocked entry point: same product, plausible clock record -------------------
 
-@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile", "streamk"])
 def test_gemm_clocked_matches_gemm(mode):
     M, N, K = 1024, 768, 512
     A, B = workloads.pair(M, N, K, "f16", "uniform", 777)
@@ -417,7 +417,7 @@ def test_gemm_clocked_rejects_short_record():
     s = ts.Schedule(mode="tiled")
     assert ts.query(M, N, K, s)["grid"] > 1
     st = ts._lib.ts_gemm_clocked(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, K, 1, N, 1, N, 1,
-                                 ts.TS_F16, ts.TS_F16, ctypes.byref(s._c()), 0, rec.data_ptr(), 1)
+                                 ts.TS_F16, ts.TS_F16, ctypes.byref(s._c()), 0, rec.data_ptr(), 1, None, 0)
     assert st == ts.TS_ERR_INVALID_ARG
 
 
@@ -425,3 +425,113 @@ def test_mfma_loop_probe_rate():
     tf = ts.mfma_loop_tflops(iters=4000, reps=2)
     say(f"mfma loop probe {tf:.1f} TFLOP/s")
     assert 200.0 < tf < 2600.0   # below the 2.4 GHz dense fp16 figure
+
+
+# ---- stream-K: split tiles, partial tiles added in a fixed order -----------------------
+
+def _streamk_run(a, b, c, sched, ws):
+    ts.gemm(a, b, out=c, schedule=sched, ws=ws)
+    torch.cuda.synchronize()
+
+
+def _streamk_ws(M, N, K, sched, ab, c_dtype):
+    q = ts.query(M, N, K, sched, ts.TS_F16 if ab == "f16" else ts.TS_BF16,
+                 {"f16": ts.TS_F16, "bf16": ts.TS_BF16, "f32": ts.TS_F32}[c_dtype])
+    header = -(-(q["grid"] + 1) * 4 // 256) * 256
+    ws = torch.zeros(max(q["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+    return q, ws, header
+
+
+def _streamk_header_clean(ws, q, header):
+    h = ws[:header].view(torch.int32).cpu()
+    assert int(h[:q["grid"]].abs().sum()) == 0, "flags not cleared"
+    assert int(h[q["grid"]]) == 0, "a stream-K wait gave up"
+
+
+@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("bf16", "f32")])
+@pytest.mark.parametrize("P", [5, 7, 64])
+def test_streamk_ragged_against_oracle(tile, ab, c_dtype, P):
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    M, N, K = 3 * bm + 17, 5 * bn + 9, 5 * bk + 11      # 4 x 6 = 24 tiles, ragged M, N, K
+    A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 640)
+    C, S = og.gemm(A, B, ab, threads=4)
+    a, b = to_device(A, ab), to_device(B, ab)
+    sched = ts.Schedule(order="grouped", group_m=3, mode="streamk", num_programs=P, xcd_remap=True, tile=tile)
+    q, ws, header = _streamk_ws(M, N, K, sched, ab, c_dtype)
+    assert q["workspace_bytes"] > 0    # 24 tiles on 5, 7 or 64 programs: 4, 3 or all 24 tiles split
+    say(f"streamk {M}x{N}x{K} {ab}->{c_dtype} {sched.label()}")
+    c1 = torch.full((M, N), float("nan"), dtype=TORCH_OUT[c_dtype], device="cuda")
+    _streamk_run(a, b, c1, sched, ws)
+    assert_accept(to_f64(c1), C, S, c_dtype, sched.label())
+    _streamk_header_clean(ws, q, header)
+    # the same again: bit-identical (partials are added in a fixed order)
+    c2 = torch.full((M, N), float("nan"), dtype=TORCH_OUT[c_dtype], device="cuda")
+    _streamk_run(a, b, c2, sched, ws)
+    assert torch.equal(c1, c2)
+    _streamk_header_clean(ws, q, header)
+
+
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+def test_streamk_integer_inputs_bit_exact(tile):
+    # exact products and sums: any split of K gives the exact result
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    for (M, N, K, P) in ((3 * bm + 5, 2 * bn + 8, 7 * bk + 8, 4), (2 * bm, 3 * bn, 6 * bk, 5), (17, 30, 8, 3)):
+        A, B = workloads.pair(M, N, K, "f16", "int", 650)
+        C, _ = og.gemm(A, B, "f16")
+        sched = ts.Schedule(order="grouped", group_m=2, mode="streamk", num_programs=P, tile=tile)
+        q, ws, header = _streamk_ws(M, N, K, sched, "f16", "f32")
+        a, b = to_device(A, "f16"), to_device(B, "f16")
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        say(f"streamk int {M}x{N}x{K} P={P} {tile}")
+        _streamk_run(a, b, c, sched, ws)
+        assert np.array_equal(to_f64(c), C), (M, N, K, P)
+        _streamk_header_clean(ws, q, header)
+
+
+def test_streamk_without_split_equals_persistent():
+    # whole rounds only: stream-K runs the persistent schedule, bit for bit
+    M, N, K = 1024, 2048, 512            # 4 x 8 tiles of 256 x 256 on 8 programs
+    A, B = workloads.pair(M, N, K, "f16", "uniform", 660)
+    a, b = to_device(A, "f16"), to_device(B, "f16")
+    s1 = ts.Schedule(order="grouped", group_m=8, mode="persistent", num_programs=8, xcd_remap=True)
+    s2 = ts.Schedule(order="grouped", group_m=8, mode="streamk", num_programs=8, xcd_remap=True)
+    assert ts.query(M, N, K, s2)["workspace_bytes"] == 0
+    c1 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    c2 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ts.gemm(a, b, out=c1, schedule=s1)
+    ts.gemm(a, b, out=c2, schedule=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+def test_streamk_ragged_bf16_full_size():
+    # the 5000 x 12290 x 1000 bf16 workload: 980 tiles of 256 x 256 on 256 programs,
+    # 212 of them split; every split tile and a sample of the others against the oracle
+    w = workloads.RAGGED_BF16
+    A, B = workloads.inputs(w)
+    a, b = to_device(A, w.ab_dtype), to_device(B, w.ab_dtype)
+    sched = ts.Schedule(order="grouped", group_m=8, mode="streamk", xcd_remap=True)
+    q, ws, header = _streamk_ws(w.M, w.N, w.K, sched, w.ab_dtype, w.c_dtype)
+    T, grid = q["num_tiles"], q["grid"]
+    assert q["workspace_bytes"] > 0 and T % grid != 0
+    say(f"streamk {w.name} {sched.label()} grid {grid}")
+    c1 = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    _streamk_run(a, b, c1, sched, ws)
+    _streamk_header_clean(ws, q, header)
+    c2 = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    _streamk_run(a, b, c2, sched, ws)
+    assert torch.equal(c1, c2)
+    from oracle import schedule as osch
+    nm, nn = q["num_m_tiles"], q["num_n_tiles"]
+    split_ids = range(T - T % grid, T)
+    tiles = {osch.grouped(t, nm, nn, 8) for t in split_ids}
+    tiles |= set(tile_sample(w.M, w.N, 256, 256, np.random.default_rng(12), n_random=32))
+    threads = max(1, min(16, og.max_threads()))
+    worst = 0.0
+    for tm, tn in sorted(tiles):
+        r0, r1 = tm * 256, min(w.M, (tm + 1) * 256)
+        c0, cc1 = tn * 256, min(w.N, (tn + 1) * 256)
+        C, S = og.gemm(A, B, w.ab_dtype, rows=(r0, r1), cols=(c0, cc1), threads=threads)
+        worst = max(worst, assert_accept(to_f64(c1[r0:r1, c0:cc1]), C, S, w.c_dtype, f"tile ({tm}, {tn})"))
+    say(f"{w.name} stream-K: {len(tiles)} tiles checked, worst |err|/bound {worst:.3g}")

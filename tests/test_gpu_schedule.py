@@ -18,7 +18,8 @@ else:
 
 def _oracle(M, N, K, s, grid):
     q = ts.query(M, N, K, s)
-    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE}[s.mode]
+    mode = {"tiled": osch.TILED, "persistent": osch.PERSISTENT, "crosstile": osch.CROSSTILE,
+            "streamk": osch.STREAMK}[s.mode]
     order = osch.GROUPED if s.order == "grouped" else osch.ROW_MAJOR
     os_ = osch.Schedule(order=order, group_m=s.group_m, mode=mode, num_programs=grid,
                         xcd_remap=s.xcd_remap, xcds=q["xcds"])
@@ -31,7 +32,7 @@ CASES = [(256, 256, 256, "64x64x32"), (5000, 12290, 1000, "256x256x64w8"), (8192
 
 @pytest.mark.parametrize("M,N,K,tile", CASES)
 @pytest.mark.parametrize("order,G", [("row_major", 8), ("grouped", 4), ("grouped", 8), ("grouped", 16)])
-@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile", "streamk"])
 @pytest.mark.parametrize("remap", [False, True])
 def test_gpu_trace_equals_oracle(M, N, K, tile, order, G, mode, remap):
     s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=0, xcd_remap=remap, tile=tile)

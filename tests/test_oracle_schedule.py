@@ -129,3 +129,61 @@ def test_trace_layout_pads_with_minus_one():
     rows = [tuple(r) for r in tr if r[0] >= 0]
     assert rows == _table("crosstile_nm2_nn3_ks2_P4.txt")
     assert (tr[tr[:, 0] < 0] == -1).all() and (tr[:, 0] < 0).sum() == 4
+
+
+# ---- stream-K split -------------------------------------------------------------------
+
+def test_streamk_hand_worked_table():
+    s = sch.Schedule(order=sch.ROW_MAJOR, mode=sch.STREAMK, num_programs=4)
+    got = []
+    for p in range(4):
+        for it, item in enumerate(sch.program_items(p, 2, 3, 3, s)):
+            got.append((p, it) + item)
+    assert got == _table("streamk_nm2_nn3_ks3_P4.txt")
+
+
+@pytest.mark.parametrize("nm,nn,ks,P", [(20, 49, 16, 256), (5, 7, 3, 4), (4, 4, 5, 100), (3, 3, 1, 2),
+                                        (2, 2, 4, 7), (8, 8, 2, 64), (1, 1, 9, 4), (7, 9, 13, 32)])
+@pytest.mark.parametrize("remap", [False, True])
+def test_streamk_coverage_and_balance(nm, nn, ks, P, remap):
+    s = sch.Schedule(order=sch.GROUPED, group_m=3, mode=sch.STREAMK, num_programs=P, xcd_remap=remap)
+    T = nm * nn
+    Pe = sch.grid_size(T, s, ks)
+    assert Pe == min(P, T * ks)
+    split = T % Pe
+    whole = T - split
+    seen, split_lens = [], []
+    for p in range(Pe):
+        items = sch.program_items(p, nm, nn, ks, s)
+        n_split = len(items) - (len(range(p if not remap else sch.xcd_remap(p, Pe), whole, Pe)) * ks)
+        split_lens.append(n_split)
+        sk = items[:n_split]
+        # a piece is contiguous in (tile id, k) order and no longer than a tile
+        assert n_split <= ks
+        ids = [(sch.grouped_table(nm, nn, 3).index(it[:2]), it[2]) for it in sk]
+        lin = [t * ks + k for t, k in ids]
+        assert lin == list(range(lin[0], lin[0] + len(lin))) if lin else True
+        assert len({t for t, _ in ids}) <= 2
+        # its whole tiles follow, each with all of its K steps in order
+        rest = items[n_split:]
+        for i in range(0, len(rest), ks):
+            assert [c[2] for c in rest[i:i + ks]] == list(range(ks))
+        seen += items
+    assert sorted(seen) == sorted((m, n, k) for m in range(nm) for n in range(nn) for k in range(ks))
+    # piece lengths differ by at most one, longer pieces on higher program indices
+    assert max(split_lens) - min(split_lens) <= 1
+    assert split_lens == sorted(split_lens)
+    assert sum(split_lens) == split * ks
+
+
+def test_streamk_without_split_is_persistent():
+    # whole rounds only (T a multiple of P), or K = 0: nothing is split
+    for nm, nn, ks, P in [(4, 4, 3, 8), (4, 4, 0, 5)]:
+        a = sch.Schedule(order=sch.GROUPED, group_m=2, mode=sch.STREAMK, num_programs=P, xcd_remap=True)
+        b = sch.Schedule(order=sch.GROUPED, group_m=2, mode=sch.PERSISTENT, num_programs=P, xcd_remap=True)
+        Pe = sch.grid_size(nm * nn, a, ks)
+        if ks == 0:
+            assert Pe == min(P, nm * nn)
+        for p in range(Pe):
+            if ks > 0 or nm * nn % Pe == 0:
+                assert sch.program_items(p, nm, nn, ks, a) == sch.program_items(p, nm, nn, ks, b) or ks == 0

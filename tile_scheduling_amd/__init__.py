@@ -31,7 +31,7 @@ _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_ALIGNMENT, TS_ERR_HIP, TS_ERR_NO_DEVICE = 0, -1, -2, -3, -4, -5
 TS_F16, TS_BF16, TS_F32 = 1, 2, 3
 ORDERS = {"row_major": 0, "grouped": 1}
-MODES = {"tiled": 0, "persistent": 1, "crosstile": 2}
+MODES = {"tiled": 0, "persistent": 1, "crosstile": 2, "streamk": 3}
 TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3, "256x256x64w8": 4}
 
 
@@ -44,7 +44,8 @@ class LaunchInfo(ctypes.Structure):
     _fields_ = [("block_m", _i32), ("block_n", _i32), ("block_k", _i32), ("threads", _i32),
                 ("num_m_tiles", _i64), ("num_n_tiles", _i64), ("k_steps", _i64), ("num_tiles", _i64),
                 ("grid", _i64), ("programs_per_cu", _i32), ("cu_count", _i32), ("xcds", _i32),
-                ("lds_bytes", _i32), ("masked", _i32), ("vgprs", _i32), ("scratch_bytes", _i32),
+                ("lds_bytes", _i32), ("masked", _i32), ("workspace_bytes", _i64), ("trace_items", _i64),
+                ("vgprs", _i32), ("scratch_bytes", _i32),
                 ("arch_vgprs", _i32), ("agprs", _i32), ("sgprs", _i32), ("spilled_vgprs", _i32),
                 ("spilled_sgprs", _i32), ("compiler_occupancy", _i32)]
 
@@ -54,7 +55,9 @@ class LaunchInfo(ctypes.Structure):
 
 _lib.ts_gemm.argtypes = [_p, _p, _p] + [_i64] * 9 + [_i32, _i32, ctypes.POINTER(_Schedule), _p]
 _lib.ts_gemm.restype = _i32
-_lib.ts_gemm_clocked.argtypes = _lib.ts_gemm.argtypes + [_p, _i64]
+_lib.ts_gemm_workspace.argtypes = _lib.ts_gemm.argtypes + [_p, _i64]
+_lib.ts_gemm_workspace.restype = _i32
+_lib.ts_gemm_clocked.argtypes = _lib.ts_gemm.argtypes + [_p, _i64, _p, _i64]
 _lib.ts_gemm_clocked.restype = _i32
 _lib.ts_mfma_loop_probe.argtypes = [_i32, _p, _i64, ctypes.POINTER(ctypes.c_double), _p]
 _lib.ts_mfma_loop_probe.restype = _i32
@@ -68,7 +71,7 @@ _lib.ts_query.restype = _i32
 _lib.ts_status_string.argtypes = [_i32]
 _lib.ts_status_string.restype = ctypes.c_char_p
 
-EXPORTS = ("ts_gemm", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
+EXPORTS = ("ts_gemm", "ts_gemm_workspace", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
            "ts_status_string", "ts_mfma_loop_probe")
 
 
@@ -88,7 +91,7 @@ class Schedule:
 
     order: str = "row_major"      # "row_major" | "grouped"
     group_m: int = 8              # GROUP_SIZE_M for the grouped order
-    mode: str = "tiled"           # "tiled" | "persistent" | "crosstile"
+    mode: str = "tiled"           # "tiled" | "persistent" | "crosstile" | "streamk"
     num_programs: int = 0         # persistent grid; 0 = CUs x workgroups per CU
     xcd_remap: bool = False       # contiguous tile-id runs per XCD
     tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64" | "256x256x64w8"
@@ -116,11 +119,29 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+_WORKSPACES: dict = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zeroed device workspace of at least ``nbytes`` for ts_gemm_workspace, one per
+    device and stream, reused by later calls (every call leaves its flags zero)."""
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def gemm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
-         out_dtype: torch.dtype | None = None, schedule: Schedule | None = None) -> torch.Tensor:
+         out_dtype: torch.dtype | None = None, schedule: Schedule | None = None,
+         ws: torch.Tensor | None = None) -> torch.Tensor:
     """C = A @ B with A [M,K], B [K,N] fp16/bf16 CUDA tensors; C fp16/bf16/fp32.
 
     Enqueued on the current stream of A's device; returns C (``out`` if given).
+    A stream-K schedule that splits tiles runs with ``ws`` (a uint8 CUDA tensor
+    of at least ``query(...)["workspace_bytes"]`` bytes whose header is zero), or
+    with a cached zeroed workspace of the device and stream.
     """
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError(f"shapes {tuple(a.shape)} @ {tuple(b.shape)} do not multiply")
@@ -132,11 +153,22 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
         out = torch.empty((M, N), dtype=out_dtype or a.dtype, device=a.device)
     elif out.shape != (M, N) or out.device != a.device:
         raise ValueError("out has the wrong shape or device")
-    s = (schedule or Schedule())._c()
-    st = _lib.ts_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
-                      a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
-                      _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0), ctypes.byref(s),
-                      _stream_handle(a.device))
+    sched = schedule or Schedule()
+    s = sched._c()
+    ab_t, c_t = _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0)
+    if sched.mode == "streamk":
+        need = query(M, N, K, sched, ab_t, c_t)["workspace_bytes"]
+        if ws is None and need > 0:
+            ws = workspace(need, a.device)
+        wptr, wbytes = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
+        st = _lib.ts_gemm_workspace(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                                    a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0),
+                                    out.stride(1), ab_t, c_t, ctypes.byref(s), _stream_handle(a.device),
+                                    wptr, wbytes)
+    else:
+        st = _lib.ts_gemm(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                          a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
+                          ab_t, c_t, ctypes.byref(s), _stream_handle(a.device))
     _check(st)
     return out
 
@@ -155,10 +187,13 @@ def gemm_clocked(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, schedule: 
     grid = query(M, N, K, sched, _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0))["grid"]
     rec = torch.zeros((max(grid, 1), 4), dtype=torch.int64, device=a.device)
     s = sched._c()
+    ab_t, c_t = _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0)
+    need = query(M, N, K, sched, ab_t, c_t)["workspace_bytes"]
+    ws = workspace(need, a.device) if need > 0 else None
     _check(_lib.ts_gemm_clocked(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
                                 a.stride(0), a.stride(1), b.stride(0), b.stride(1), out.stride(0), out.stride(1),
-                                _TORCH_DTYPE.get(a.dtype, 0), _TORCH_DTYPE.get(out.dtype, 0), ctypes.byref(s),
-                                _stream_handle(a.device), rec.data_ptr(), rec.shape[0]))
+                                ab_t, c_t, ctypes.byref(s), _stream_handle(a.device), rec.data_ptr(), rec.shape[0],
+                                ws.data_ptr() if ws is not None else None, need))
     return rec
 
 
@@ -217,9 +252,8 @@ def schedule_trace(M: int, N: int, K: int, schedule: Schedule | None = None,
                    ab_dtype: int = TS_F16, c_dtype: int = TS_F16, device: int | str = "cuda"):
     """GPU-computed work sequence of every workgroup, as an int32 [rows, 5] CPU tensor."""
     info = query(M, N, K, schedule, ab_dtype, c_dtype)
-    ksp = max(info["k_steps"], 1)
     grid = info["grid"]
-    rows = grid * (-(-info["num_tiles"] // grid) * ksp if grid else 0)
+    rows = grid * info["trace_items"]
     out = torch.empty((max(rows, 1), 5), dtype=torch.int32, device=device)
     s = (schedule or Schedule())._c()
     _check(_lib.ts_schedule_trace(M, N, K, ab_dtype, c_dtype, ctypes.byref(s), out.data_ptr(), rows,
@@ -241,8 +275,7 @@ def schedule_trace_host(M: int, N: int, K: int, schedule: Schedule, cu_count: in
     if schedule.mode != "tiled" and schedule.num_programs == 0:
         sized = dataclasses.replace(schedule, num_programs=cu_count * programs_per_cu)
     info = query(M, N, K, sized, ab_dtype, c_dtype)
-    grid, T = info["grid"], info["num_tiles"]
-    rows = grid * (-(-T // grid) * max(info["k_steps"], 1)) if grid else 0
+    rows = info["grid"] * info["trace_items"]
     out = np.full((max(rows, 1), 5), -7, dtype=np.int32)
     s = schedule._c()
     _check(_lib.ts_schedule_trace_host(M, N, K, ab_dtype, c_dtype, ctypes.byref(s), cu_count,

@@ -77,7 +77,7 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
 }
 
 KernelRef kernel_of(const Plan& p) {
-    const bool edge = p.path == PATH_EDGE16 || p.path == PATH_EDGE4;   // only on direct-to-LDS tiles
+    const bool edge = p.path == PATH_EDGE;   // only on direct-to-LDS tiles
     switch (p.cfg) {
         case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, p.mode);
         case CFG_128: return edge ? kernels_cfg128_edge(p.io, p.path, p.mode) : kernels_cfg128(p.io, p.path, p.mode);
@@ -96,18 +96,17 @@ bool cfg_has_fast_path(int cfg) {
 }
 
 // Kernel path of a plan.  A masked plan runs the direct-to-LDS pipeline with
-// zero-filled edges when every load of it lies wholly inside or wholly outside
-// A and B: A's base 16-byte aligned with K and its row stride multiples of 8
-// elements; B's base, row stride and N multiples of 16 bytes (16-byte loads) or of
-// 4 bytes (4-byte loads); and the in-tile offsets below 2^30 bytes.  Otherwise the
-// masked register pipeline runs.
+// zero-filled edges when A's base is 16-byte aligned with K and its row stride
+// multiples of 8 elements (a 16-byte chunk of A never mixes the end of a row
+// with the next row), B's base is 4-byte aligned with N and its row stride even
+// (no dword straddles the end of B), and the in-tile offsets stay below 2^30
+// bytes.  Otherwise the masked register pipeline runs.
 int choose_path(const Plan& p, int64_t N, int64_t K, uintptr_t a, uintptr_t b, int64_t lda, int64_t ldb) {
     if (!p.masked) return PATH_FULL;
     if (!cfg_has_fast_path(p.cfg) || K <= 0 || K % 8 != 0) return PATH_MASKED;
     if (a % 16 != 0 || lda % 8 != 0) return PATH_MASKED;
     if ((int64_t)p.bm * lda * 2 >= (1LL << 30) || (int64_t)p.bk * ldb * 2 >= (1LL << 30)) return PATH_MASKED;
-    if (b % 16 == 0 && ldb % 8 == 0 && N % 8 == 0) return PATH_EDGE16;
-    if (b % 4 == 0 && ldb % 2 == 0 && N % 2 == 0) return PATH_EDGE4;
+    if (b % 4 == 0 && ldb % 2 == 0 && N % 2 == 0) return PATH_EDGE;
     return PATH_MASKED;
 }
 
@@ -147,7 +146,8 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     if (sp) s = *sp;
     if (s.order != TS_ORDER_ROW_MAJOR && s.order != TS_ORDER_GROUPED) return TS_ERR_INVALID_ARG;
     if (s.order == TS_ORDER_GROUPED && s.group_m < 1) return TS_ERR_INVALID_ARG;
-    if (s.mode != TS_MODE_TILED && s.mode != TS_MODE_PERSISTENT && s.mode != TS_MODE_CROSSTILE)
+    if (s.mode != TS_MODE_TILED && s.mode != TS_MODE_PERSISTENT && s.mode != TS_MODE_CROSSTILE &&
+        s.mode != TS_MODE_STREAMK)
         return TS_ERR_INVALID_ARG;
     if (s.num_programs < 0) return TS_ERR_INVALID_ARG;
     if (s.xcd_remap != 0 && s.xcd_remap != 1) return TS_ERR_INVALID_ARG;
@@ -210,6 +210,7 @@ ts_status resolve_grid(Plan* p, int cu_count, int ppc, int xcds) {
         p->max_items = 0;
         return TS_OK;
     }
+    const int64_t ksp = p->s.ks > 0 ? p->s.ks : 1;
     if (p->mode == TS_MODE_TILED) {
         p->s.grid = p->s.num_tiles;
     } else {
@@ -218,11 +219,32 @@ ts_status resolve_grid(Plan* p, int cu_count, int ppc, int xcds) {
             if (cu_count <= 0 || ppc <= 0) return TS_ERR_NO_DEVICE;
             P = (int64_t)cu_count * ppc;
         }
-        p->s.grid = (int)(P < p->s.num_tiles ? P : p->s.num_tiles);
+        // persistent: at most one program per tile; stream-K: per (tile, K step) item
+        const int64_t cap = p->mode == TS_MODE_STREAMK ? (int64_t)p->s.num_tiles * ksp : p->s.num_tiles;
+        p->s.grid = (int)(P < cap ? P : cap);
     }
-    const int64_t ksp = p->s.ks > 0 ? p->s.ks : 1;
-    p->max_items = cdiv64(p->s.num_tiles, p->s.grid) * ksp;
+    if (p->mode == TS_MODE_STREAMK) {
+        const StreamK sk(p->s);
+        p->max_items = cdiv64(sk.dp_tiles, p->s.grid) * ksp + sk.q + (sk.rem > 0 ? 1 : 0);
+    } else {
+        p->max_items = cdiv64(p->s.num_tiles, p->s.grid) * ksp;
+    }
     return TS_OK;
+}
+
+// Stream-K workspace of a resolved plan: a header of one flag per range plus an
+// error counter (rounded up to 256 bytes), then one fp32 partial tile per range.
+// Zero when the launch splits no tile.
+struct WorkspaceLayout {
+    int64_t header, part_bytes, total;
+};
+WorkspaceLayout workspace_layout(const Plan& p) {
+    WorkspaceLayout w{0, 0, 0};
+    if (p.mode != TS_MODE_STREAMK || p.s.grid == 0 || StreamK(p.s).sk_items == 0) return w;
+    w.header = ((int64_t)(p.s.grid + 1) * 4 + 255) / 256 * 256;
+    w.part_bytes = (int64_t)p.bm * p.bn * 4;
+    w.total = w.header + (int64_t)p.s.grid * w.part_bytes;
+    return w;
 }
 
 }  // namespace
@@ -242,10 +264,15 @@ extern "C" const char* ts_status_string(ts_status status) {
     return "unknown ts_status";
 }
 
+// Sleeps (s_sleep 2, about 128 clocks each) before a stream-K wait gives up:
+// about 2^24 * 128 clocks, roughly a second at the clocks the GEMM runs.
+constexpr int kStreamKSpin = 1 << 24;
+
 static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                              int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
                              int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
-                             const ts_schedule* sched, void* stream, uint64_t* clock_out, int64_t clock_rows) {
+                             const ts_schedule* sched, void* stream, uint64_t* clock_out, int64_t clock_rows,
+                             void* workspace, int64_t workspace_bytes) {
     Plan p;
     ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
     if (st != TS_OK) return st;
@@ -275,14 +302,27 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     if ((int64_t)p.bm * stride_am * 2 > INT_MAX || (int64_t)p.bk * stride_bk * 2 > INT_MAX) p.masked = 1;
     p.path = choose_path(p, N, K, a, b, stride_am, stride_bk);
 
+    auto workspace_ok = [&](const Plan& q) {
+        const WorkspaceLayout w = workspace_layout(q);
+        return w.total == 0 || (workspace && workspace_bytes >= w.total && ((uintptr_t)workspace % 256) == 0);
+    };
+    const bool grid_needs_device = p.mode != TS_MODE_TILED && p.requested_programs == 0;
+    if (!grid_needs_device) {   // the workspace check needs no device here: report it first
+        Plan q = p;
+        st = resolve_grid(&q, 0, 0, 8);
+        if (st != TS_OK) return st;
+        if (!workspace_ok(q)) return TS_ERR_INVALID_ARG;
+    }
     int dev;
     DeviceInfo di;
     st = current_device(&dev, &di);
     if (st != TS_OK) return st;
-    const int ppc = (p.mode != TS_MODE_TILED && p.requested_programs == 0) ? programs_per_cu(p) : 1;
+    const int ppc = grid_needs_device ? programs_per_cu(p) : 1;
     st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
     if (st != TS_OK) return st;
     if (clock_out && clock_rows < p.s.grid) return TS_ERR_INVALID_ARG;
+    if (!workspace_ok(p)) return TS_ERR_INVALID_ARG;
+    const WorkspaceLayout wl = workspace_layout(p);
 
     GemmArgs g;
     g.A = static_cast<const uint16_t*>(A);
@@ -307,6 +347,10 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     g.b_bytes = K > 0 ? ((K - 1) * stride_bk + N) * 2 : 0;
     g.s = p.s;
     g.clk = reinterpret_cast<unsigned long long*>(clock_out);
+    g.sk_flags = wl.total > 0 ? static_cast<int*>(workspace) : nullptr;
+    g.sk_err = wl.total > 0 ? static_cast<int*>(workspace) + p.s.grid : nullptr;
+    g.sk_part = wl.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.header) : nullptr;
+    g.sk_spin = kStreamKSpin;
     const KernelRef k = kernel_of(p);
     void* args[] = {&g};
     if (hipLaunchKernel(k.fn, dim3(p.s.grid), dim3(k.threads), args, 0, (hipStream_t)stream) != hipSuccess) {
@@ -321,17 +365,27 @@ extern "C" ts_status ts_gemm(const void* A, const void* B, void* C, int64_t M, i
                              int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
                              const ts_schedule* sched, void* stream) {
     return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
-                       ab_dtype, c_dtype, sched, stream, nullptr, 0);
+                       ab_dtype, c_dtype, sched, stream, nullptr, 0, nullptr, 0);
+}
+
+extern "C" ts_status ts_gemm_workspace(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                       int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                                       int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
+                                       const ts_schedule* sched, void* stream, void* workspace,
+                                       int64_t workspace_bytes) {
+    if (workspace_bytes < 0) return TS_ERR_INVALID_ARG;
+    return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       ab_dtype, c_dtype, sched, stream, nullptr, 0, workspace, workspace_bytes);
 }
 
 extern "C" ts_status ts_gemm_clocked(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                                      int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
                                      int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
                                      const ts_schedule* sched, void* stream, uint64_t* clock_out,
-                                     int64_t clock_rows) {
-    if (!clock_out) return TS_ERR_INVALID_ARG;
+                                     int64_t clock_rows, void* workspace, int64_t workspace_bytes) {
+    if (!clock_out || workspace_bytes < 0) return TS_ERR_INVALID_ARG;
     return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
-                       ab_dtype, c_dtype, sched, stream, clock_out, clock_rows);
+                       ab_dtype, c_dtype, sched, stream, clock_out, clock_rows, workspace, workspace_bytes);
 }
 
 extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
@@ -361,6 +415,8 @@ extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
     out->xcds = p.s.xcds;
     out->lds_bytes = k.lds_bytes;
     out->masked = p.path;
+    out->workspace_bytes = workspace_layout(p).total;
+    out->trace_items = p.max_items;
     out->vgprs = -1;
     out->scratch_bytes = -1;
     const KernelResources* kr = resources_of(k.fn);

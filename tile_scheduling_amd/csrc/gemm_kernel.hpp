@@ -50,6 +50,7 @@ namespace ts {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -75,6 +76,11 @@ struct GemmArgs {
     long long a_bytes, b_bytes;  // bytes from A (B) to the end of its last element
     SchedArgs s;
     unsigned long long* clk;  // null, or 4 values per program (see ProgramClock)
+    // stream-K workspace (MODE_STREAMK launches that split tiles; see StreamK)
+    float* sk_part;           // one partial tile (BM x BN fp32) per range
+    int* sk_flags;            // one flag per range: 1 = its partial tile is written
+    int* sk_err;              // incremented when a wait for a flag gives up
+    int sk_spin;              // sleeps before a wait gives up
 };
 
 // Optional per-program clock record: shader-clock counter (s_memtime) and the
@@ -273,13 +279,13 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
 // Kernel paths: whole tiles; masked register pipeline; direct-to-LDS pipeline with
-// ragged edges, its B loads 16 bytes (EDGE16) or 4 bytes (EDGE4) per lane.
-enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE16 = 2, PATH_EDGE4 = 3 };
+// ragged edges zero-filled by the loads' range checks.
+enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE = 2 };
 
 template <class Cfg, class TI, class TO, int PATH>
 struct Engine {
     static constexpr bool MASKED = PATH == PATH_MASKED;
-    static constexpr bool EDGE = PATH == PATH_EDGE16 || PATH == PATH_EDGE4;
+    static constexpr bool EDGE = PATH == PATH_EDGE;
     static constexpr bool EDGES = PATH != PATH_FULL;   // C stores masked to M x N
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH, SUB = Cfg::SUB;
@@ -299,8 +305,7 @@ struct Engine {
     static_assert(!EDGE || FAST, "the edge paths run the direct-to-LDS pipeline");
     static constexpr int BH = RBB / 256;                                // 256-byte pieces of a B row
     static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
-    static constexpr int B_DMA_N = !FAST ? 0 : PATH == PATH_EDGE4 ? BK * BH / NW   // 256-byte B loads per wave
-                                                                  : BK * RBB / 1024 / NW;  // 1 KiB B loads per wave
+    static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
     static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
     static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
     static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
@@ -498,13 +503,15 @@ struct Engine {
     }
 
     // Buffer resource over the slice at element offset `off` of A (B): on the edge
-    // paths its record count stops at the matrix's last element, so that rows past
+    // path its record count stops at the matrix's last element, so that rows past
     // M (K) and columns past the end read as zero.  Every offset of those loads is
-    // in the per-lane offset, which the range check covers, and every load lies
-    // wholly inside or wholly outside the range (the edge paths need K, lda and the
-    // base (N, ldb and the base) to be multiples of the load size).
-    // The count is clamped to [0, 2^31 - 16], a multiple of every load size; the
-    // in-tile offsets of the edge paths stay below 2^30.
+    // in the per-lane offset, which the range check covers; the check is made per
+    // dword, so each dword of a load reads either its data or zero (A: K, lda and
+    // the base are multiples of 8 elements, so a chunk never mixes the last k of a
+    // row with the next row; B: N, ldb and the base are even / 4-byte aligned, so
+    // no dword straddles the end of B).
+    // The count is clamped to [0, 2^31 - 16], a multiple of 4; the in-tile offsets
+    // of the edge path stay below 2^30.
     static __device__ __forceinline__ int clamp_records(long long left) {
         return (int)(left < 0 ? 0 : left < 0x7ffffff0LL ? left : 0x7ffffff0LL);
     }
@@ -539,28 +546,20 @@ struct Engine {
 #pragma unroll
         for (int c = 0; c < A_DMA_N; ++c) dma_a_one<SLOT>(c, r);
     }
-    // Fast path: B load number c of this wave, into B slot `slot`: 1 KiB (16 bytes a
-    // lane), or on PATH_EDGE4 256 bytes (4 bytes a lane) of one row, placed in the
-    // same swizzled image: lane l's dword lands at byte 4 l of its 256-byte piece,
-    // i.e. in chunk l/4 of the piece, which holds logical chunk (l/4) ^ f(k).
+    // Fast path: B load number c of this wave (1 KiB, 16 bytes a lane), into B slot
+    // `slot`.  On the edge path B's rows need only be 4-byte aligned: a 16-byte
+    // buffer load needs no more than dword alignment, and the range check of a raw
+    // buffer load is made per dword (both checked on MI355X with an in-bounds probe),
+    // so a load that straddles the end of B returns its dwords before the end and
+    // zeros after it.
     template <int SLOT>
     __device__ __forceinline__ void dma_b_one(int c, const __amdgpu_buffer_rsrc_t& r) {
-        if constexpr (PATH == PATH_EDGE4) {
-            const int idx = c * NW + wave;                 // 256-byte piece of the slice
-            const int kr = idx / BH, h = idx % BH;          // its row and its place in the row
-            const int f = (4 * (kr & 3)) ^ (2 * ((kr >> 3) & 1));
-            const uint32_t voff = (((uint32_t)lane * 4) ^ (uint32_t)(16 * f)) + (uint32_t)(h * 256) +
-                                  (uint32_t)(kr * (int)g.ldb * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(lb[SLOT] + kr * RBB + h * 256), 4, (int)voff, 0, 0, 0);
-        } else {
-            const int grp = c * NW + wave;                 // RPD-row group (1 KiB)
-            const int e = ((c * NW * RPD) >> 3) & 1;
-            if constexpr (EDGE)
-                dma16(r, b_dg[e] + (uint32_t)(grp * RPD * (int)g.ldb * 2), 0, lb[SLOT] + grp * 1024);
-            else
-                dma16(r, b_dg[e], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
-        }
+        const int grp = c * NW + wave;                 // RPD-row group (1 KiB)
+        const int e = ((c * NW * RPD) >> 3) & 1;
+        if constexpr (EDGE)
+            dma16(r, b_dg[e] + (uint32_t)(grp * RPD * (int)g.ldb * 2), 0, lb[SLOT] + grp * 1024);
+        else
+            dma16(r, b_dg[e], (int)((long long)grp * RPD * g.ldb * 2), lb[SLOT] + grp * 1024);
     }
     template <int SLOT>
     __device__ __forceinline__ void dma_b(int n0, int k, int valid) {
@@ -932,25 +931,91 @@ struct Engine {
         if (FAST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // Full pipeline for one tile (no epilogue): steps alternate B slots 0 and 1; an
-    // odd step count runs one slot-0 step first and then pairs starting on slot 1.
-    __device__ __forceinline__ void tile_mainloop(int m0, int n0, int ks) {
-        prologue(Next{m0, 0, -1, n0, 0, -1}, Next{m0, 1, vmask(1, ks), n0, 1, vmask(1, ks)});
+    // Full pipeline over K steps [k0, k1) of one tile (no epilogue): steps alternate
+    // B slots 0 and 1; an odd step count runs one slot-0 step first and then pairs
+    // starting on slot 1.
+    __device__ __forceinline__ void tile_mainloop(int m0, int n0, int k0, int k1) {
+        prologue(Next{m0, k0, -1, n0, k0, -1},
+                 Next{m0, k0 + 1, vmask(k0 + 1, k1), n0, k0 + 1, vmask(k0 + 1, k1)});
         auto nx = [&](int k) {  // loads of step k
-            return Next{m0, k + DA, vmask(k + DA, ks), n0, k + DB, vmask(k + DB, ks)};
+            return Next{m0, k + DA, vmask(k + DA, k1), n0, k + DB, vmask(k + DB, k1)};
         };
-        int k = 0;
-        if (ks & 1) {
-            kstep<0>(nx(0));
-            for (k = 1; k < ks; k += 2) {
+        int k = k0;
+        if ((k1 - k0) & 1) {
+            kstep<0>(nx(k0));
+            for (k = k0 + 1; k < k1; k += 2) {
                 kstep<1>(nx(k));
                 kstep<0>(nx(k + 1));
             }
         } else {
-            for (; k < ks; k += 2) {
+            for (; k < k1; k += 2) {
                 kstep<0>(nx(k));
                 kstep<1>(nx(k + 1));
             }
+        }
+    }
+
+    // Stream-K partial tile: the fp32 accumulators in register order, threads
+    // interleaved -- float4 number u = (i * FN + j) * 4 + q of thread tid (its
+    // accumulator block (i, j), values 4q .. 4q + 3) at index u * NT + tid -- so
+    // that every store and load of a wave moves 1 KiB of consecutive bytes and the
+    // owner of the tile reads back exactly the values its own registers hold.
+    // Partial tiles move between XCDs, whose L2s are not coherent with each other:
+    // they are written and read with device-scope cache policy (sc1: written through
+    // the L2 and read past it), like the device-scope atomics, so that publishing
+    // one needs only the writes to complete, not a write-back of the whole L2.
+    // Buffer accesses: the per-lane offset is the same for every access and the
+    // block offset goes in the scalar offset, so that no per-access address
+    // registers are needed beside the accumulators.
+    static constexpr int PART_FLOATS = BM * BN;
+    static constexpr int kDeviceScope = 16;   // cache policy bit sc1
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* part) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(part), (short)0, PART_FLOATS * 4, kBufferFlags);
+    }
+    __device__ __forceinline__ void write_partial(float* part) const {
+        const __amdgpu_buffer_rsrc_t r = part_rsrc(part);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // whole-vector casts only: a bit cast of one element of a vector
+                    // value is not reliable in this compiler (it reads element 0)
+                    const f32x4 f = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f), r, tid * 16,
+                                                           ((i * FN + j) * 4 + q) * NT * 16, kDeviceScope);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+    // Partial tiles first .. last of a split tile, added in the epilogue (the
+    // accumulators themselves are not changed, which keeps them in place).
+    struct Parts {
+        const float* base;   // partial tile 0
+        int first, last;     // none if first > last
+    };
+    // v[0..3] (float4 number u of this thread) += partial tiles first .. last, in
+    // order; two partial tiles' loads are in flight at a time.
+    __device__ __forceinline__ void add_parts(float* v, const Parts& pt, int u, int t) const {
+        int c = pt.first;
+        for (; c + 1 <= pt.last; c += 2) {
+            const f32x4 p0 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(pt.base + (long long)c * PART_FLOATS), t * 16,
+                                                             u * NT * 16, kDeviceScope));
+            const f32x4 p1 = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(pt.base + (long long)(c + 1) * PART_FLOATS),
+                                                             t * 16, u * NT * 16, kDeviceScope));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (v[e] + p0[e]) + p1[e];
+        }
+        if (c <= pt.last) {
+            const f32x4 p = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_rsrc(pt.base + (long long)c * PART_FLOATS), t * 16,
+                                                             u * NT * 16, kDeviceScope));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += p[e];
         }
     }
 
@@ -1005,13 +1070,16 @@ struct Engine {
     }
     static __device__ __forceinline__ int stage_swz(int r) { return (CPR == 8 ? (r >> 1) : r) & (CPR - 1); }
 
-    __device__ __forceinline__ void store_tile_staged(int m0, int n0) {
+    template <bool PARTS>
+    __device__ __forceinline__ void store_tile_staged(int m0, int n0, const Parts& pt) {
         // The lane index passes through an opaque copy here, so the per-lane
         // addresses below are formed at the store; otherwise, where the epilogue sits
         // inside a K loop, they are hoisted out of it and held in registers through
         // every step.
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        int tt = tid;
+        if (PARTS) asm volatile("" : "+v"(tt));
         const int r32 = ln & 31, hk = ln >> 5;
         char* st = ldsc + wave * Cfg::STAGE_W;
         OutT* C = reinterpret_cast<OutT*>(g.C);
@@ -1031,6 +1099,7 @@ struct Engine {
                             char* dst = st + r * ROWB + ch * 16 + (byte & 15);
                             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                           acc[i][j][4 * q + 3]};
+                            if (PARTS) add_parts(v, pt, (i * FN + j) * 4 + q, tt);
                             Out<TO>::store4(reinterpret_cast<OutT*>(dst), v, 4, true);
                         }
                     }
@@ -1053,10 +1122,12 @@ struct Engine {
         }
     }
 
-    // Accumulators -> C (round to the output type), masked to M x N.
-    __device__ __forceinline__ void store_tile(int m0, int n0) {
+    // Accumulators (plus, with PARTS, the partial tiles of pt) -> C (round to the
+    // output type), masked to M x N.
+    template <bool PARTS = false>
+    __device__ __forceinline__ void store_tile(int m0, int n0, const Parts& pt = Parts{nullptr, 0, -1}) {
         if constexpr (STAGED) {
-            store_tile_staged(m0, n0);
+            store_tile_staged<PARTS>(m0, n0, pt);
             return;
         }
         typedef typename Out<TO>::T T;
@@ -1074,6 +1145,7 @@ struct Engine {
                     const int n = n0 + wn * Cfg::TN + j * 32 + 8 * q + 4 * hk;
                     float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                   acc[i][j][4 * q + 3]};
+                    if (PARTS) add_parts(v, pt, (i * FN + j) * 4 + q, tid);
                     if (!MASKED) {
                         Out<TO>::store4(crow + n, v, 4, true);
                     } else {
@@ -1091,25 +1163,103 @@ struct Engine {
 
 // ---- kernels -------------------------------------------------------------------------
 
-// Tiled and persistent modes: for each of the program's tiles, a full pipeline
-// (prologue loads, K loop with two slices in flight, epilogue).
+// Stream-K fix-up of a split tile (MODE_STREAMK; see StreamK).  The range holding
+// K step 0 of a tile finishes it: it waits until every later range of the tile
+// (r + 1 .. last) has published its partial tile, and its epilogue adds them to its
+// own accumulators in range order (a fixed order, so the result is the same on
+// every run) before storing C.  Any other piece publishes its accumulators as the
+// range's partial tile -- device-scope writes, completed before the flag is set --
+// and raises the range's flag; the finishing range clears the flag again, so the
+// flags are zero between launches.  A range publishes before it waits for
+// anything, and only ranges of lower program index are waited for, so the waits
+// end once those programs run; a wait that exceeds sk_spin sleeps still gives up
+// (counted in sk_err).
+template <class E>
+__device__ __forceinline__ void streamk_publish(E& e, const GemmArgs& g, int r) {
+    e.write_partial(g.sk_part + (long long)r * E::PART_FLOATS);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // written through to device scope
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(g.sk_flags + r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits for the flags of ranges r + 1 .. last and clears them; the partial tiles
+// are then read (device scope) by the epilogue.
+__device__ __forceinline__ void streamk_wait(const GemmArgs& g, int r, int last) {
+    if (threadIdx.x == 0) {
+        for (int c = r + 1; c <= last; ++c) {
+            int n = 0;
+            while (__hip_atomic_load(g.sk_flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++n > g.sk_spin) {
+                    __hip_atomic_fetch_add(g.sk_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            __hip_atomic_store(g.sk_flags + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __syncthreads();
+}
+
+// Tiled, persistent and stream-K modes: for each of the program's work pieces, a
+// full pipeline (prologue loads, K loop with two slices in flight, epilogue).  A
+// piece is a whole tile, or in stream-K mode first the (at most two) pieces of
+// the program's range of split tiles.  One loop runs every kind of piece, so the
+// K loop is instantiated once.
 template <class Cfg, class TI, class TO, int PATH, int MODE>
 __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
-    Engine<Cfg, TI, TO, PATH> e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
+    typedef Engine<Cfg, TI, TO, PATH> E;
+    E e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
     ProgramClock pc;
     pc.start(g);
-    const ProgramWork w(g.s, blockIdx.x);
+    const int ks = g.s.ks;
+    // stream-K range of this program: items [b, end) of the split tiles
+    int limit = g.s.num_tiles, r = 0, b = 0, end = 0;
+    StreamK sk(g.s);
+    if constexpr (MODE == MODE_STREAMK) {
+        limit = sk.dp_tiles;
+        r = sk.range_of_program(g.s, blockIdx.x);
+        b = sk.range_begin(r);
+        end = sk.range_begin(r + 1);
+    }
+    const ProgramWork w(g.s, blockIdx.x, limit);
     const int ntiles = (MODE == MODE_TILED) ? 1 : w.ntiles;
-    for (int i = 0; i < ntiles; ++i) {
+    for (int i = 0;;) {
+        int tile, k0 = 0, k1 = ks;
+        bool split = false;
+        if (MODE == MODE_STREAMK && b < end) {
+            const int t = b / ks;
+            tile = sk.dp_tiles + t;
+            k0 = b - t * ks;
+            k1 = k0 + (end - b) < ks ? k0 + (end - b) : ks;
+            split = k0 > 0 || k1 < ks;
+            b += k1 - k0;
+        } else if (i < ntiles) {
+            tile = w.tile_id(i++);
+        } else {
+            break;
+        }
         int tm, tn;
-        tile_coords(g.s, w.tile_id(i), tm, tn);
+        tile_coords(g.s, tile, tm, tn);
         const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
         e.zero_acc();
-        if (PATH != PATH_MASKED || g.s.ks > 0) e.tile_mainloop(m0, n0, g.s.ks);
-        e.store_tile(m0, n0);
+        if (PATH != PATH_MASKED || ks > 0) e.tile_mainloop(m0, n0, k0, k1);
+        if constexpr (MODE == MODE_STREAMK) {
+            typename E::Parts pt{g.sk_part, r + 1, r};   // none
+            if (split) {
+                if (k0 > 0) {
+                    streamk_publish(e, g, r);
+                    continue;
+                }
+                pt.last = sk.range_of((tile - sk.dp_tiles + 1) * ks - 1);
+                streamk_wait(g, r, pt.last);
+            }
+            e.template store_tile<true>(m0, n0, pt);
+        } else {
+            e.store_tile(m0, n0);
+        }
     }
     e.drain();
     pc.stop(g);

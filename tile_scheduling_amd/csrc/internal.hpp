@@ -37,6 +37,7 @@ const void* kernel_by_mode(int mode) {
     switch (mode) {
         case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_TILED>);
         case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_PERSISTENT>);
+        case MODE_STREAMK: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_STREAMK>);
         default:
             if constexpr (has_flat_kernel<Cfg>())
                 return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);
@@ -55,9 +56,9 @@ const void* kernel_by_path_base(int path, int mode) {
 }
 template <class Cfg, class TI, class TO>
 const void* kernel_by_path_edge(int path, int mode) {
-    static_assert(Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK, "edge paths need the direct-to-LDS pipeline");
-    return path == PATH_EDGE16 ? kernel_by_mode<Cfg, TI, TO, PATH_EDGE16>(mode)
-                               : kernel_by_mode<Cfg, TI, TO, PATH_EDGE4>(mode);
+    static_assert(Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK, "the edge path needs the direct-to-LDS pipeline");
+    (void)path;
+    return kernel_by_mode<Cfg, TI, TO, PATH_EDGE>(mode);
 }
 
 template <class Cfg, class TI, class TO, bool EDGE>
@@ -90,7 +91,7 @@ KernelRef kernels_cfg64(int io, int path, int mode);
 KernelRef kernels_cfg128(int io, int path, int mode);
 KernelRef kernels_cfg256(int io, int path, int mode);
 KernelRef kernels_cfg256w8(int io, int path, int mode);
-// path PATH_EDGE16 or PATH_EDGE4 (configurations with the direct-to-LDS pipeline)
+// path PATH_EDGE (configurations with the direct-to-LDS pipeline)
 KernelRef kernels_cfg128_edge(int io, int path, int mode);
 KernelRef kernels_cfg256_edge(int io, int path, int mode);
 KernelRef kernels_cfg256w8_edge(int io, int path, int mode);

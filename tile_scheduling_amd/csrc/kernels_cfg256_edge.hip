@@ -1,5 +1,5 @@
 // Zero-filled-edge kernel instances of the 256 tile configuration (every mode
-// and type pair; B in 16-byte or 4-byte pieces).
+// and type pair).
 #include "internal.hpp"
 
 namespace ts {

@@ -18,6 +18,9 @@
 //   flattened cross-tile ("(3/n) ... cross tile pipelining"): the same ids and K
 //     steps as persistent, walked as one loop whose counter k wraps to 0 after
 //     the last K step of a tile.
+//   stream-K (the follow-on the persistent page names; the split below is this
+//     library's design): the tiles of the last, partial round of the persistent
+//     grid are cut along K and spread evenly over all P programs (see StreamK).
 // XCD remap (this library's addition; not on the pages): MI355X deals the
 //   workgroups of a launch round-robin over its 8 XCDs, each with a private L2.
 //   Renumbering w -> (w % X) * q + min(w % X, r) + w / X (q = n / X, r = n % X)
@@ -36,7 +39,7 @@
 namespace ts {
 
 enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
-enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2 };
+enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2, MODE_STREAMK = 3 };
 
 // Everything a program needs to find its tiles.  Plain integers, passed by value
 // to kernels.  `group_m` is already clamped to [1, nm] by the host (values above
@@ -80,23 +83,56 @@ TS_HD void tile_coords(const SchedArgs& s, int t, int& tm, int& tn) {
     }
 }
 
-// The work of one program: tile ids start, start + grid, ... below num_tiles,
-// each with max(ks, 1) K steps.  ks == 0 (K == 0) keeps one step per tile so
-// that the tile is still written (with zeros).
+// The work of one program: tile ids start, start + grid, ... below `limit`
+// (num_tiles, or the whole-tile part of a stream-K launch), each with max(ks, 1)
+// K steps.  ks == 0 (K == 0) keeps one step per tile so that the tile is still
+// written (with zeros).
 struct ProgramWork {
     int start;   // first logical tile id
     int step;    // distance between consecutive tile ids of this program
     int ntiles;  // tiles this program computes
     int ksp;     // K steps per tile, at least 1
 
-    TS_HD ProgramWork(const SchedArgs& s, int program) {
+    TS_HD ProgramWork(const SchedArgs& s, int program) : ProgramWork(s, program, s.num_tiles) {}
+    TS_HD ProgramWork(const SchedArgs& s, int program, int limit) {
         start = s.remap ? xcd_remap(program, s.grid, s.xcds) : program;
         step = s.grid;
-        ntiles = start < s.num_tiles ? cdiv_i(s.num_tiles - start, s.grid) : 0;
+        ntiles = start < limit ? cdiv_i(limit - start, s.grid) : 0;
         ksp = s.ks > 0 ? s.ks : 1;
     }
     TS_HD int tile_id(int i) const { return start + i * step; }
     TS_HD int total_items() const { return ntiles * ksp; }
+};
+
+// Stream-K split of a launch of P = grid programs over T tiles of ks K steps.
+// The first dp_tiles = T - (T mod P) tile ids (whole rounds of the persistent
+// grid) are computed whole, persistent style.  The remaining T mod P tiles form
+// sk_items = (T mod P) * ks (tile, K step) items, numbered tile-major from tile
+// id dp_tiles, k ascending inside a tile; they are dealt as P contiguous ranges
+// whose lengths differ by at most one (the first `rem` ranges one longer).
+// Program p takes range r = P - 1 - p, so that a tile's ranges run from a higher
+// program index (the range holding K step 0, which finishes the tile) down to
+// lower ones.  No range is longer than a tile (the split tiles number fewer than
+// P), so a range touches at most two tiles.  With ks == 0 nothing is split.
+struct StreamK {
+    int dp_tiles;   // tiles computed whole
+    int sk_items;   // (tile, K step) items of the split tiles
+    int q, rem;     // range r holds q + (r < rem) items
+
+    TS_HD explicit StreamK(const SchedArgs& s) {
+        const int sk_tiles = (s.ks > 0 && s.grid > 0) ? s.num_tiles % s.grid : 0;
+        dp_tiles = s.num_tiles - sk_tiles;
+        sk_items = sk_tiles * s.ks;
+        q = s.grid > 0 ? sk_items / s.grid : 0;
+        rem = s.grid > 0 ? sk_items - q * s.grid : 0;
+    }
+    TS_HD int range_begin(int r) const { return r * q + min_i(r, rem); }
+    // range holding item i (0 <= i < sk_items)
+    TS_HD int range_of(int i) const {
+        const int big = rem * (q + 1);
+        return i < big ? i / (q + 1) : rem + (i - big) / q;
+    }
+    TS_HD int range_of_program(const SchedArgs& s, int program) const { return s.grid - 1 - program; }
 };
 
 // Cursor of the flattened loop: (tile id, k) advanced one K step at a time;
@@ -120,8 +156,31 @@ struct FlatCursor {
 // padded with -1.  The nested walk is used for tiled and persistent modes, the
 // flattened cursor for the cross-tile mode, exactly as the kernels do.
 TS_HD void trace_program(const SchedArgs& s, int mode, int program, int max_items, int32_t* rows) {
-    const ProgramWork w(s, program);
     int it = 0;
+    if (mode == MODE_STREAMK) {
+        // the split items of this program's range first, then its whole tiles
+        const StreamK sk(s);
+        const int r = sk.range_of_program(s, program);
+        for (int i = sk.range_begin(r), e = sk.range_begin(r + 1); i < e; ++i, ++it) {
+            int tm, tn;
+            tile_coords(s, sk.dp_tiles + i / s.ks, tm, tn);
+            int32_t* row = rows + 5 * it;
+            row[0] = program; row[1] = it; row[2] = tm; row[3] = tn; row[4] = i % s.ks;
+        }
+        const ProgramWork w(s, program, sk.dp_tiles);
+        for (int i = 0; i < w.ntiles; ++i) {
+            int tm, tn;
+            tile_coords(s, w.tile_id(i), tm, tn);
+            for (int k = 0; k < w.ksp; ++k, ++it) {
+                int32_t* row = rows + 5 * it;
+                row[0] = program; row[1] = it; row[2] = tm; row[3] = tn; row[4] = k;
+            }
+        }
+        for (; it < max_items; ++it)
+            for (int f = 0; f < 5; ++f) rows[5 * it + f] = -1;
+        return;
+    }
+    const ProgramWork w(s, program);
     if (mode == MODE_CROSSTILE) {
         FlatCursor c(w);
         for (int n = w.total_items(); it < n; ++it) {
