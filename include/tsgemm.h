@@ -189,6 +189,32 @@ ts_status ts_gemm_workspace(const void* A, const void* B, void* C,
                             void* workspace, int64_t workspace_bytes);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ts_gemm_workspace without
+ * a workspace argument.  A launch that needs a workspace (TS_MODE_STREAMK with
+ * split tiles) uses this library's own scratch array instead, a static device
+ * array of ts_noalloc_scratch_bytes() bytes (64 MiB + 64 KiB) of which every GPU
+ * the library runs on holds one copy until the process ends; a launch that would
+ * need more returns TS_ERR_UNSUPPORTED before any HIP call (query workspace_bytes
+ * first).  The call allocates nothing: before the GEMM it enqueues one small
+ * kernel that clears the scratch array's flags.  Every call on a GPU shares that
+ * GPU's array, so calls that overlap in time on one GPU (on different streams,
+ * or from different threads) race and must not be made.  Otherwise as
+ * ts_gemm_workspace; launches that need no workspace behave exactly as ts_gemm.
+ */
+ts_status ts_gemm_noalloc(const void* A, const void* B, void* C,
+                          int64_t M, int64_t N, int64_t K,
+                          int64_t stride_am, int64_t stride_ak,
+                          int64_t stride_bk, int64_t stride_bn,
+                          int64_t stride_cm, int64_t stride_cn,
+                          int32_t ab_dtype, int32_t c_dtype,
+                          const ts_schedule* sched, void* stream);
+
+/* Size in bytes of the scratch array ts_gemm_noalloc uses (the largest workspace
+   it accepts). */
+int64_t ts_noalloc_scratch_bytes(void);
+
+/*
  * This library's own addition, for measurement: ts_gemm with a clock record: the same product, launch and
  * errors, and in addition thread 0 of every workgroup p writes four counters to
  * the device buffer clock_out (owned by the caller, clock_rows x 4 uint64):

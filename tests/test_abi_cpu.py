@@ -207,3 +207,14 @@ def test_streamk_needs_its_workspace():
     assert ts._lib.ts_gemm_workspace(*args, FAKE, need - 1) == ts.TS_ERR_INVALID_ARG
     assert ts._lib.ts_gemm_workspace(*args, FAKE + 16, need) == ts.TS_ERR_INVALID_ARG
     assert ts._lib.ts_gemm_workspace(*args, FAKE, -1) == ts.TS_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_oversize_launches_before_any_hip_call():
+    cap = ts._lib.ts_noalloc_scratch_bytes()
+    assert cap == (64 << 20) + (64 << 10)
+    big = ts.Schedule(mode="streamk", num_programs=8191, tile="64x64x32")
+    assert ts.query(4096, 4096, 512, big)["workspace_bytes"] > cap
+    assert ts._lib.ts_gemm_noalloc(FAKE, FAKE, FAKE, 4096, 4096, 512, 512, 1, 4096, 1, 4096, 1, ts.TS_F16,
+                                   ts.TS_F16, ctypes.byref(big._c()), None) == ts.TS_ERR_UNSUPPORTED
+    small = ts.Schedule(mode="streamk", num_programs=256, tile="256x256x64w8")
+    assert 0 < ts.query(5000, 12290, 1000, small, ts.TS_BF16, ts.TS_F32)["workspace_bytes"] <= cap

@@ -57,6 +57,10 @@ _lib.ts_gemm.argtypes = [_p, _p, _p] + [_i64] * 9 + [_i32, _i32, ctypes.POINTER(
 _lib.ts_gemm.restype = _i32
 _lib.ts_gemm_workspace.argtypes = _lib.ts_gemm.argtypes + [_p, _i64]
 _lib.ts_gemm_workspace.restype = _i32
+_lib.ts_gemm_noalloc.argtypes = list(_lib.ts_gemm.argtypes)
+_lib.ts_gemm_noalloc.restype = _i32
+_lib.ts_noalloc_scratch_bytes.argtypes = []
+_lib.ts_noalloc_scratch_bytes.restype = _i64
 _lib.ts_gemm_clocked.argtypes = _lib.ts_gemm.argtypes + [_p, _i64, _p, _i64]
 _lib.ts_gemm_clocked.restype = _i32
 _lib.ts_mfma_loop_probe.argtypes = [_i32, _p, _i64, ctypes.POINTER(ctypes.c_double), _p]
@@ -71,7 +75,7 @@ _lib.ts_query.restype = _i32
 _lib.ts_status_string.argtypes = [_i32]
 _lib.ts_status_string.restype = ctypes.c_char_p
 
-EXPORTS = ("ts_gemm", "ts_gemm_workspace", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
+EXPORTS = ("ts_gemm", "ts_gemm_workspace", "ts_gemm_noalloc", "ts_noalloc_scratch_bytes", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
            "ts_status_string", "ts_mfma_loop_probe")
 
 

@@ -16,6 +16,18 @@
 
 namespace ts {
 
+// Scratch memory of ts_gemm_noalloc: the stream-K workspace for callers that cannot
+// allocate.  One copy per GPU, held until the process ends.  Host code never uses
+// this name as an address: the device address comes from hipGetSymbolAddress,
+// once per device (scratch_ptr below).
+constexpr int64_t kScratchBytes = (64ll << 20) + (64 << 10);
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Sets n words at p to zero (the flags of a stream-K workspace).
+__global__ void clear_words(int* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 __global__ void trace_kernel(SchedArgs s, int mode, int max_items, int32_t* out) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p < s.grid) trace_program(s, mode, p, max_items, out + (long long)p * max_items * 5);
@@ -32,6 +44,22 @@ struct DeviceInfo {
 
 std::once_flag g_dev_once[kMaxDevices];
 DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];          // device address of `scratch` on each device
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's copy of `scratch` (dev must be current).
+ts_status scratch_ptr(int dev, void** out) {
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+        g_scratch[dev] = ptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch[dev]) return TS_ERR_HIP;
+    *out = g_scratch[dev];
+    return TS_OK;
+}
 
 // Properties of the current device, queried once per device.
 ts_status current_device(int* dev_out, DeviceInfo* info) {
@@ -268,11 +296,13 @@ extern "C" const char* ts_status_string(ts_status status) {
 // about 2^24 * 128 clocks, roughly a second at the clocks the GEMM runs.
 constexpr int kStreamKSpin = 1 << 24;
 
+// use_scratch: the workspace is this library's per-device scratch array (the
+// caller passes none); a launch that needs more than kScratchBytes is refused.
 static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                              int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
                              int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
                              const ts_schedule* sched, void* stream, uint64_t* clock_out, int64_t clock_rows,
-                             void* workspace, int64_t workspace_bytes) {
+                             void* workspace, int64_t workspace_bytes, bool use_scratch = false) {
     Plan p;
     ts_status st = plan_shape(M, N, K, ab_dtype, c_dtype, sched, &p);
     if (st != TS_OK) return st;
@@ -302,16 +332,19 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     if ((int64_t)p.bm * stride_am * 2 > INT_MAX || (int64_t)p.bk * stride_bk * 2 > INT_MAX) p.masked = 1;
     p.path = choose_path(p, N, K, a, b, stride_am, stride_bk);
 
-    auto workspace_ok = [&](const Plan& q) {
+    auto workspace_check = [&](const Plan& q) -> ts_status {
         const WorkspaceLayout w = workspace_layout(q);
-        return w.total == 0 || (workspace && workspace_bytes >= w.total && ((uintptr_t)workspace % 256) == 0);
+        if (use_scratch) return w.total <= kScratchBytes ? TS_OK : TS_ERR_UNSUPPORTED;
+        return (w.total == 0 || (workspace && workspace_bytes >= w.total && ((uintptr_t)workspace % 256) == 0))
+                   ? TS_OK : TS_ERR_INVALID_ARG;
     };
     const bool grid_needs_device = p.mode != TS_MODE_TILED && p.requested_programs == 0;
     if (!grid_needs_device) {   // the workspace check needs no device here: report it first
         Plan q = p;
         st = resolve_grid(&q, 0, 0, 8);
         if (st != TS_OK) return st;
-        if (!workspace_ok(q)) return TS_ERR_INVALID_ARG;
+        st = workspace_check(q);
+        if (st != TS_OK) return st;
     }
     int dev;
     DeviceInfo di;
@@ -321,8 +354,19 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
     if (st != TS_OK) return st;
     if (clock_out && clock_rows < p.s.grid) return TS_ERR_INVALID_ARG;
-    if (!workspace_ok(p)) return TS_ERR_INVALID_ARG;
+    st = workspace_check(p);
+    if (st != TS_OK) return st;
     const WorkspaceLayout wl = workspace_layout(p);
+    if (use_scratch && wl.total > 0) {
+        st = scratch_ptr(dev, &workspace);
+        if (st != TS_OK) return st;
+        // the array keeps the last call's contents: clear the flags and the timeout
+        // counter (a fill kernel, so that the call can be captured in a graph)
+        const int words = (int)(wl.header / 4);
+        hipLaunchKernelGGL(clear_words, dim3((words + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                           static_cast<int*>(workspace), words);
+        if (hipGetLastError() != hipSuccess) return TS_ERR_HIP;
+    }
 
     GemmArgs g;
     g.A = static_cast<const uint16_t*>(A);
@@ -377,6 +421,16 @@ extern "C" ts_status ts_gemm_workspace(const void* A, const void* B, void* C, in
     return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
                        ab_dtype, c_dtype, sched, stream, nullptr, 0, workspace, workspace_bytes);
 }
+
+extern "C" ts_status ts_gemm_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                     int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,
+                                     int64_t stride_cm, int64_t stride_cn, int32_t ab_dtype, int32_t c_dtype,
+                                     const ts_schedule* sched, void* stream) {
+    return gemm_launch(A, B, C, M, N, K, stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn,
+                       ab_dtype, c_dtype, sched, stream, nullptr, 0, nullptr, 0, true);
+}
+
+extern "C" int64_t ts_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" ts_status ts_gemm_clocked(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                                      int64_t stride_am, int64_t stride_ak, int64_t stride_bk, int64_t stride_bn,

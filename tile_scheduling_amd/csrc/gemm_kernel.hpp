@@ -489,9 +489,13 @@ struct Engine {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
                                                  __builtin_amdgcn_readfirstlane(nrec), kBufferFlags);
     }
-    // -1 if k < lim, else 0 (for 0 <= k, lim < 2^30)
+    // -1 if k < lim, else 0 (for 0 <= k, lim < 2^30).  RFL: k and lim are
+    // wave-uniform but the compiler's divergence analysis cannot see it (in the
+    // stream-K kernel, whose fix-up wait is a branch taken by one lane), so the
+    // difference goes through readfirstlane.
+    template <bool RFL = false>
     static __device__ __forceinline__ int vmask(int k, int lim) {
-        int d = k - lim;
+        int d = RFL ? __builtin_amdgcn_readfirstlane(k - lim) : k - lim;
         asm("" : "+s"(d));  // opaque: keeps the shift from being folded back into a compare and select
         return d >> 31;
     }
@@ -934,11 +938,12 @@ struct Engine {
     // Full pipeline over K steps [k0, k1) of one tile (no epilogue): steps alternate
     // B slots 0 and 1; an odd step count runs one slot-0 step first and then pairs
     // starting on slot 1.
+    template <bool RFL = false>
     __device__ __forceinline__ void tile_mainloop(int m0, int n0, int k0, int k1) {
         prologue(Next{m0, k0, -1, n0, k0, -1},
-                 Next{m0, k0 + 1, vmask(k0 + 1, k1), n0, k0 + 1, vmask(k0 + 1, k1)});
+                 Next{m0, k0 + 1, vmask<RFL>(k0 + 1, k1), n0, k0 + 1, vmask<RFL>(k0 + 1, k1)});
         auto nx = [&](int k) {  // loads of step k
-            return Next{m0, k + DA, vmask(k + DA, k1), n0, k + DB, vmask(k + DB, k1)};
+            return Next{m0, k + DA, vmask<RFL>(k + DA, k1), n0, k + DB, vmask<RFL>(k + DB, k1)};
         };
         int k = k0;
         if ((k1 - k0) & 1) {
@@ -1245,7 +1250,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_tiles_kernel(GemmArgs g) {
         tile_coords(g.s, tile, tm, tn);
         const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
         e.zero_acc();
-        if (PATH != PATH_MASKED || ks > 0) e.tile_mainloop(m0, n0, k0, k1);
+        if (PATH != PATH_MASKED || ks > 0) e.template tile_mainloop<MODE == MODE_STREAMK>(m0, n0, k0, k1);
         if constexpr (MODE == MODE_STREAMK) {
             typename E::Parts pt{g.sk_part, r + 1, r};   // none
             if (split) {
