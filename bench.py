@@ -10,15 +10,18 @@ last hardware-counter profile measured for this kernel source, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME]
-                    [--sweep] [--ksweep] [--extras] [--pmc-target | --stall-target]
+                    [--sweep] [--ksweep] [--extras] [--pps-sweep] [--index-ablation]
+                    [--pmc-target | --stall-target | --target mix|ksweep|ragged]
 
 --sweep times every order x remap x mode at the workload; --ksweep times the
 grouped persistent loop against the flattened cross-tile loop over the K sweep
 at 16384 x 16384; --extras times the benchmarked launch hot and cold, the 8192
 grid, the ragged bf16 workload and one GPU's share of an eight-way row split,
 and the oracle on one host thread (tables on stderr, before the JSON line).
---pmc-target and --stall-target only run the fixed launch sequences that the
-hardware-counter passes profile.
+--pps-sweep times one and two workgroups per CU for the 128x128x64 tile;
+--index-ablation times the tile-order maps by division against multiply-shift.
+--pmc-target, --stall-target and --target only run the fixed launch sequences
+that the hardware-counter passes profile.
 
 Schedules are written order[+remap]/mode[/P<programs>][/tile], e.g.
 "grouped8+remap/tiled", "rowmajor/persistent/P256", "grouped8/crosstile".
@@ -41,7 +44,7 @@ PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 MFMA_TFLOPS_PER_GHZ = 256 * 4 * 1024 / 1000.0   # 256 CUs x 4 SIMDs x 1024 FLOP/clk, per GHz
 PEAK_HBM_GBS = 8000.0    # MI355X HBM3E
 METRIC = "fp16 GEMM TFLOPS (2MNK/s) + % MFMA peak at M=N=16384, K=4096"
-DEFAULT_SCHEDULE = "grouped8+remap/persistent"
+DEFAULT_SCHEDULE = "auto/auto"   # order, G, remap and mode chosen by the library per shape
 KERNEL_SOURCES = ["tile_scheduling_amd/csrc/gemm_kernel.hpp", "tile_scheduling_amd/csrc/schedule.hpp",
                   "tile_scheduling_amd/csrc/internal.hpp"]
 
@@ -59,19 +62,32 @@ def parse_schedule(text: str):
     order_s = order_s.replace("+remap", "")
     if order_s in ("rowmajor", "row_major"):
         order, G = "row_major", 8
+    elif order_s in ("auto", "autoorder"):
+        order, G = "auto", 8
     else:
         m = re.fullmatch(r"grouped(\d+)", order_s)
         if not m:
             raise ValueError(f"bad order {order_s!r}")
         order, G = "grouped", int(m.group(1))
     mode = parts[1] if len(parts) > 1 else "tiled"
-    P, tile = 0, "auto"
+    P, tile, index_math = 0, "auto", "divide"
     for extra in parts[2:]:
         if extra.startswith("P"):
             P = int(extra[1:])
+        elif extra in ("mulshift", "divide"):
+            index_math = extra
         else:
             tile = extra
-    return ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
+    return ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile,
+                       index_math=index_math)
+
+
+def resolved_label(q) -> str:
+    """The schedule ts_query resolved (auto order and mode replaced by the choice)."""
+    o = f"grouped{q['group_m']}" if q["order"] == 1 else "rowmajor"
+    r = "+remap" if q["xcd_remap"] else ""
+    m = {0: "tiled", 1: "persistent", 2: "crosstile", 3: "streamk"}[q["mode"]]
+    return f"{o}{r}/{m}"
 
 
 def sources_sha() -> str:
@@ -219,6 +235,102 @@ def stall_target(ts, torch, np, workloads):
             print(f"dispatch gemm {w.name} {s.label()} rep{rep}", flush=True)
 
 
+def _device_inputs(ts, torch, np, w):
+    A, B = __import__("workloads").inputs(w)
+    in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
+    out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.c_dtype]
+    a = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
+    b = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
+    c = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
+    return a, b, c
+
+
+# Launch sequences for the other counter passes (`--target NAME`): each runs the
+# listed (workload, schedule) launches `reps` times, synchronising after each, and
+# prints one manifest line per dispatch, so that the profile's dispatch rows can
+# be matched to schedules.
+TARGETS = {
+    # instruction mix: one tile per workgroup against the persistent loop, with the
+    # tile-order maps by integer division and by multiply-shift
+    "mix": [(w, f"grouped8+remap/{m}{x}") for w in ("gemm_4096x4096x4096_f16", "gemm_16384x16384x4096_f16")
+            for m in ("tiled", "persistent") for x in ("", "/mulshift")],
+    # the K sweep: grouped persistent against the flattened cross-tile loop
+    "ksweep": [(f"gemm_16384x16384x{k}_f16_ksweep", f"grouped8+remap/{m}") for k in (128, 512, 1024, 2048, 4096)
+               for m in ("persistent", "crosstile")],
+    # the ragged bf16 product: persistent, cross-tile and stream-K on the edge path
+    "ragged": [("gemm_5000x12290x1000_bf16_f32", f"grouped8+remap/{m}") for m in ("persistent", "crosstile",
+                                                                                  "streamk")],
+}
+
+
+def scaling_dispatches(torch):
+    """A 1 GiB fill and a 1 GiB copy (known HBM bytes, to scale FETCH_SIZE and
+    WRITE_SIZE), each announced by a manifest line."""
+    n = 1 << 29  # 2-byte elements: 1 GiB per buffer
+    x = torch.empty(n, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    torch.cuda.synchronize()
+    print("dispatch fill 1073741824 write", flush=True)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print("dispatch copy 1073741824 read+write", flush=True)
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def run_target(ts, torch, np, workloads, name, reps=3):
+    by_name = {w.name: w for w in workloads.ALL}
+    scaling_dispatches(torch)
+    loaded = {}
+    for wname, lab in TARGETS[name]:
+        if wname not in loaded:
+            loaded.clear()
+            torch.cuda.empty_cache()
+            loaded[wname] = _device_inputs(ts, torch, np, by_name[wname])
+        a, b, c = loaded[wname]
+        s = parse_schedule(lab)
+        for rep in range(reps):
+            ts.gemm(a, b, out=c, schedule=s)
+            torch.cuda.synchronize()
+            print(f"dispatch gemm {wname} {s.label()} rep{rep}", flush=True)
+
+
+def pps_sweep(ts, torch, np, workloads, steps):
+    """Programs per CU (the persistent page's programs_per_sm): the 128 x 128 x 64
+    tile (two workgroups fit a CU) with P = CUs x 1 and CUs x 2, against its tiled
+    launch, at 4096^3 and 16384^2 x 4096 (stderr table)."""
+    cus = ts.query(256, 256, 256)["cu_count"]
+    for wname in ("gemm_4096x4096x4096_f16", "gemm_16384x16384x4096_f16"):
+        w = {x.name: x for x in workloads.ALL}[wname]
+        a, b, c = _device_inputs(ts, torch, np, w)
+        flops = 2.0 * w.M * w.N * w.K
+        for lab in ["grouped8+remap/tiled/128x128x64"] + \
+                   [f"grouped8+remap/persistent/P{cus * k}/128x128x64" for k in (1, 2)] + \
+                   ["grouped8+remap/persistent/256x256x64w8"]:
+            s = parse_schedule(lab)
+            r = time_gemm(ts, torch, a, b, c, s, steps, 10)
+            q = ts.query(w.M, w.N, w.K, s)
+            log(f"pps {wname} {lab:44s} grid {q['grid']:5d} ({q['programs_per_cu']} per CU fit)  "
+                f"median {r['median_ms']:.4f} ms  {flops / r['median_ms'] / 1e9:8.1f} TFLOP/s")
+        del a, b, c
+
+
+def index_ablation(ts, torch, np, workloads, steps):
+    """Tile-order maps by integer division against multiply-shift (stderr table)."""
+    for wname in ("gemm_4096x4096x4096_f16", "gemm_16384x16384x4096_f16", "gemm_16384x16384x128_f16_ksweep"):
+        w = {x.name: x for x in workloads.ALL}[wname]
+        a, b, c = _device_inputs(ts, torch, np, w)
+        flops = 2.0 * w.M * w.N * w.K
+        for m in ("tiled", "persistent", "crosstile"):
+            for x in ("", "/mulshift"):
+                lab = f"grouped8+remap/{m}{x}"
+                r = time_gemm(ts, torch, a, b, c, parse_schedule(lab), steps, 10)
+                log(f"index {wname} {lab:36s} median {r['median_ms']:.4f} ms (p90 {r['p90_ms']:.4f})  "
+                    f"{flops / r['median_ms'] / 1e9:8.1f} TFLOP/s")
+        del a, b, c
+
+
 KSWEEP_SCHEDULES = ("grouped8+remap/persistent", "grouped8+remap/crosstile")
 
 
@@ -232,10 +344,10 @@ def ksweep(ts, torch, np, workloads, steps):
         flops = 2.0 * w.M * w.N * w.K
         hbm = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N)   # compulsory bytes, fp16
         for lab in KSWEEP_SCHEDULES:
-            r = time_gemm(ts, torch, a, b, c, parse_schedule(lab), steps, 3)
+            r = time_gemm(ts, torch, a, b, c, parse_schedule(lab), steps, 10)
             t = r["median_ms"] * 1e-3
-            log(f"ksweep K={w.K:5d} {lab:28s} median {r['median_ms']:.4f} ms  {flops / t / 1e12:8.1f} TFLOP/s  "
-                f"compulsory {hbm / t / 1e9:7.1f} GB/s")
+            log(f"ksweep K={w.K:5d} {lab:28s} median {r['median_ms']:.4f} ms (min {r['min_ms']:.4f}, "
+                f"p90 {r['p90_ms']:.4f})  {flops / t / 1e12:8.1f} TFLOP/s  compulsory {hbm / t / 1e9:7.1f} GB/s")
         del a, b, c
 
 
@@ -317,6 +429,12 @@ def main():
                     help="run the fixed launch sequence used for hardware-counter passes and exit")
     ap.add_argument("--stall-target", action="store_true",
                     help="run the launch sequence of the wave-state counter passes and exit")
+    ap.add_argument("--target", choices=sorted(TARGETS),
+                    help="run one of the other counter-pass launch sequences and exit")
+    ap.add_argument("--pps-sweep", action="store_true",
+                    help="also time programs per CU 1 and 2 for the 128x128x64 tile (stderr table)")
+    ap.add_argument("--index-ablation", action="store_true",
+                    help="also time the tile maps by integer division against multiply-shift (stderr table)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -337,6 +455,9 @@ def main():
     if args.stall_target:
         stall_target(ts, torch, np, workloads)
         return
+    if args.target:
+        run_target(ts, torch, np, workloads, args.target)
+        return
     w = by_name[args.workload]
     out_dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.c_dtype]
     in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
@@ -349,6 +470,10 @@ def main():
 
     if args.ksweep:
         ksweep(ts, torch, np, workloads, max(10, args.steps))
+    if args.pps_sweep:
+        pps_sweep(ts, torch, np, workloads, max(10, args.steps))
+    if args.index_ablation:
+        index_ablation(ts, torch, np, workloads, max(10, args.steps))
     if args.extras:
         extras(ts, torch, np, workloads, a, b, c, w, parse_schedule(args.schedule), max(10, args.steps))
     if args.sweep:
@@ -388,7 +513,7 @@ def main():
     clock["frac_of_loop_peak"] = round(achieved / loop_peak, 4)
     log(f"clock {clock}")
 
-    traffic = measured_traffic(w.name, sched.label())
+    traffic = measured_traffic(w.name, resolved_label(q))
     # Roofline of the workload: compulsory bytes (A and B read once, C written once)
     # against 2MNK; below the ridge point (peak FLOP/s over peak bytes/s) the kernel
     # is bound by HBM and is reported against the HBM roof.
@@ -416,6 +541,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.ab_dtype, "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.ab_dtype, "acc": "f32",
                    "out": w.c_dtype, "inputs": f"{w.dist} seed {w.seed}", "schedule": sched.label(),
+                   "resolved_schedule": resolved_label(q),
                    "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "threads": q["threads"],
                    "grid": q["grid"], "kernel_path": q["masked"],
                    "executed_tflops": round(executed * args.steps / r["wall_s"] / 1e12, 2)},

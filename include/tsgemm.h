@@ -55,7 +55,18 @@ enum {
     /* grouped ordering / CTA swizzle: ids walk GROUP_SIZE_M tile rows at a time,
        M coordinate first; the last group holds the remaining num_m_tiles mod G
        rows ("(2/n) ... grouped ordering (CTA swizzle)", section Implementation) */
-    TS_ORDER_GROUPED = 1
+    TS_ORDER_GROUPED = 1,
+    /* chosen per shape by the library (group_m and xcd_remap are ignored): among
+       row-major and grouped orders with G in {2, 4, 8, 16, 32}, each with and
+       without the XCD remap, the one whose first round of workgroups touches the
+       fewest distinct tile rows and tile columns per XCD (a model of L2 reuse:
+       each XCD has its own L2); ties go to the earlier candidate in the order
+       G=8+remap, G=4+remap, G=16+remap, row-major, row-major+remap, G=8, G=4,
+       G=16, G=2+remap, G=32+remap, G=2, G=32.  The grouping page's closing
+       section says the best order depends on the size and the cache; this is
+       that choice made from a model rather than a sweep.  ts_query reports the
+       resolved order, G and remap. */
+    TS_ORDER_AUTO = 2
 };
 
 /* how workgroups take tiles */
@@ -78,7 +89,19 @@ enum {
        from run to run but not bit-identical to the other modes (a different
        summation order along K).  Needs a workspace: ts_gemm_workspace, sized by
        ts_query's workspace_bytes (0 when no tile is split). */
-    TS_MODE_STREAMK = 3
+    TS_MODE_STREAMK = 3,
+    /* chosen by the library: TS_MODE_CROSSTILE when a tile has at most 16 K
+       steps (the cross-tile page finds the merged loop paying where the tile
+       boundary is a large share of the work, i.e. at small K), else
+       TS_MODE_PERSISTENT.  ts_query reports the resolved mode. */
+    TS_MODE_AUTO = 4
+};
+
+/* index arithmetic of the tile-order maps */
+enum {
+    TS_INDEX_DIVIDE = 0,     /* integer division and remainder                            */
+    TS_INDEX_MULSHIFT = 1    /* multiply-high and shift by multipliers made on the host
+                                (Granlund and Montgomery 1994); the same map, bit for bit */
 };
 
 /* tile configurations (BLOCK_M x BLOCK_N x BLOCK_K) */
@@ -102,6 +125,7 @@ typedef struct {
     int32_t xcd_remap;     /* 1 = renumber workgroups so that each XCD (chiplet with its own
                               L2) works on one contiguous run of tile ids; 0 = off             */
     int32_t tile_config;   /* TS_TILE_*                                                       */
+    int32_t index_math;    /* TS_INDEX_*                                                      */
 } ts_schedule;
 
 typedef struct {
@@ -133,6 +157,11 @@ typedef struct {
     int32_t spilled_vgprs;              /* vector registers spilled to private memory          */
     int32_t spilled_sgprs;              /* scalar registers spilled                            */
     int32_t compiler_occupancy;         /* waves per SIMD the compiler computed                */
+    /* the schedule as resolved (TS_ORDER_AUTO / TS_MODE_AUTO replaced by the choice) */
+    int32_t order, group_m, mode, xcd_remap, index_math;
+    int32_t model_l2_reuse_pm;          /* the L2 model's reuse fraction of the resolved order,
+                                           in 1/1000: 1 - distinct tile rows and columns per
+                                           XCD over 2 x tiles, in the first round          */
 } ts_launch_info;
 
 /*

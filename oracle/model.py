@@ -22,6 +22,12 @@ floor(available / per-block) blocks, waves = grid / (SMs * blocks per SM).
 For ragged shapes the tiled read count keeps only in-bounds elements (masked
 loads fetch nothing): sum over tiles of K * (rows + cols) = K * (nn*M + nm*N).
 
+The per-XCD L2 locality model at the end of this file is this library's own
+(not on the pages): the pages' reuse-distance argument ("(2/n) ...", section
+"Reuse distance and cache capacity") moved to a GPU whose XCDs each have their
+own L2.  It is pinned by hand-worked cases and by the reuse fractions computed
+for the tile grids of the 16384 x 16384 product when the build was planned.
+
 Parity pins: every number the notes and pages print for these quantities
 (tests/test_oracle_model.py).
 """
@@ -130,3 +136,49 @@ def tiles_per_program(num_tiles: int, P: int):
     lo = num_tiles // P
     extra = num_tiles % P
     return lo, lo + (1 if extra else 0), (extra if extra else P)
+
+
+# ---- per-XCD L2 locality model (this library's own) ------------------------------------
+
+def l2_locality(nm: int, nn: int, grid: int, concurrent: int, xcds: int, order: str, G: int, remap: bool):
+    """(cost, tiles): the first min(concurrent, grid) workgroups of a launch, workgroup
+    w on XCD w mod xcds, each on the first tile of its schedule; cost = distinct
+    (XCD, tile row) pairs + distinct (XCD, tile column) pairs.  Reuse = 1 - cost /
+    (2 * tiles): the share of panel requests an XCD's L2 could serve from another
+    tile in the same round."""
+    from oracle import schedule as sch
+
+    T = nm * nn
+    rows, cols = set(), set()
+    tiles = 0
+    for w in range(min(concurrent, grid)):
+        start = sch.xcd_remap(w, grid, xcds) if remap else w
+        if start >= T:
+            continue
+        tm, tn = sch.grouped(start, nm, nn, G) if order == "grouped" else sch.row_major(start, nm, nn)
+        rows.add((w % xcds, tm))
+        cols.add((w % xcds, tn))
+        tiles += 1
+    return len(rows) + len(cols), tiles
+
+
+AUTO_ORDER_CANDIDATES = (("grouped", 8, True), ("grouped", 4, True), ("grouped", 16, True),
+                         ("row_major", 1, False), ("row_major", 1, True), ("grouped", 8, False),
+                         ("grouped", 4, False), ("grouped", 16, False), ("grouped", 2, True),
+                         ("grouped", 32, True), ("grouped", 2, False), ("grouped", 32, False))
+
+
+def choose_order(nm: int, nn: int, grid: int, concurrent: int, xcds: int = 8):
+    """The candidate (order, G, remap) of least locality cost, ties to the earlier
+    candidate; grouped candidates with G > nm are skipped (same map as G = nm).
+    Returns (order, G, remap, reuse in 1/1000, integer part)."""
+    best = None
+    for order, G, remap in AUTO_ORDER_CANDIDATES:
+        if order == "grouped" and G > nm:
+            continue
+        cost, tiles = l2_locality(nm, nn, grid, concurrent, xcds, order, G, remap)
+        if best is None or cost < best[0]:
+            best = (cost, tiles, order, G, remap)
+    cost, tiles, order, G, remap = best
+    reuse_pm = (1000 - (1000 * cost) // (2 * tiles)) if tiles else 0
+    return order, G, remap, reuse_pm

@@ -68,7 +68,8 @@ def test_invalid_arguments_are_rejected(kw, expect):
 def test_bad_schedule_enums_are_rejected():
     s = ts._Schedule(5, 1, 0, 0, 0, 0)
     assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(s), None) == -1
-    for bad in (ts._Schedule(0, 1, 4, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9)):
+    for bad in (ts._Schedule(0, 1, 5, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9),
+                ts._Schedule(3, 1, 0, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 0, 0, 2)):
         assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(bad), None) == -1
 
 
@@ -218,3 +219,50 @@ def test_noalloc_refuses_oversize_launches_before_any_hip_call():
                                    ts.TS_F16, ctypes.byref(big._c()), None) == ts.TS_ERR_UNSUPPORTED
     small = ts.Schedule(mode="streamk", num_programs=256, tile="256x256x64w8")
     assert 0 < ts.query(5000, 12290, 1000, small, ts.TS_BF16, ts.TS_F32)["workspace_bytes"] <= cap
+
+
+# ---- per-shape schedule choice (TS_ORDER_AUTO, TS_MODE_AUTO) ---------------------------
+
+@pytest.mark.parametrize("M,N,K,tile,mode,P", [
+    (16384, 16384, 4096, "256x256x64w8", "persistent", 256), (8192, 8192, 4096, "256x256x64w8", "persistent", 256),
+    (5000, 12290, 1000, "256x256x64w8", "tiled", 0), (5000, 12290, 1000, "256x256x64w8", "persistent", 256),
+    (16384, 16384, 4096, "128x128x64", "persistent", 512), (2048, 16384, 4096, "256x256x64w8", "tiled", 0),
+    (4096, 4096, 4096, "128x128x64", "tiled", 0), (1000, 64000, 512, "128x128x64", "persistent", 300),
+    (3000, 700, 256, "64x64x32", "tiled", 0)])
+def test_auto_order_is_the_models_choice(M, N, K, tile, mode, P):
+    from oracle import model as om
+
+    q = ts.query(M, N, K, ts.Schedule(order="auto", mode=mode, num_programs=P, tile=tile))
+    # without a device the library takes 256 resident workgroups
+    concurrent = min(256, q["grid"])
+    order, G, remap, pm = om.choose_order(q["num_m_tiles"], q["num_n_tiles"], q["grid"], concurrent, 8)
+    got = ("grouped" if q["order"] == 1 else "row_major", q["group_m"] if q["order"] == 1 else 1,
+           bool(q["xcd_remap"]))
+    assert got == (order, G, remap)
+    assert q["model_l2_reuse_pm"] == pm
+    # the trace of the resolved schedule equals the oracle's for it
+    sched = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
+    auto = ts.Schedule(order="auto", mode=mode, num_programs=P, tile=tile)
+    if q["grid"] * q["trace_items"] <= 300000:
+        assert np.array_equal(ts.schedule_trace_host(M, N, K, auto), ts.schedule_trace_host(M, N, K, sched))
+
+
+@pytest.mark.parametrize("K,expect", [(128, "crosstile"), (1024, "crosstile"), (1025, "persistent"),
+                                      (4096, "persistent"), (0, "crosstile")])
+def test_auto_mode_by_k_steps(K, expect):
+    q = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256, tile="256x256x64w8"))
+    assert q["mode"] == {"persistent": 1, "crosstile": 2}[expect]
+    # the 4-wave 256 tile has no cross-tile kernel: auto falls back to persistent
+    q = ts.query(16384, 16384, 128, ts.Schedule(mode="auto", num_programs=256, tile="256x256x64"))
+    assert q["mode"] == 1
+
+
+@pytest.mark.parametrize("order,G", [("row_major", 1), ("grouped", 3), ("grouped", 8), ("grouped", 100)])
+@pytest.mark.parametrize("M,N", [(5000, 12290), (16384, 16384), (333, 290), (70000, 300)])
+def test_mulshift_index_math_gives_the_same_map(order, G, M, N):
+    for mode, P in (("persistent", 256), ("crosstile", 7), ("tiled", 0), ("streamk", 256)):
+        a = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=True, tile="128x128x64")
+        b = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=True, tile="128x128x64",
+                        index_math="mulshift")
+        assert ts.query(M, N, 256, b)["index_math"] == 1
+        assert np.array_equal(ts.schedule_trace_host(M, N, 256, a), ts.schedule_trace_host(M, N, 256, b))

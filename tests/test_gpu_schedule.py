@@ -50,3 +50,31 @@ def test_device_properties_and_auto_grid():
     assert q["cu_count"] > 0 and q["programs_per_cu"] >= 1
     assert q["grid"] == min(q["cu_count"] * q["programs_per_cu"], q["num_tiles"])
     assert q["scratch_bytes"] >= 0 and q["vgprs"] > 0
+
+
+@pytest.mark.parametrize("M,N,K,tile", CASES)
+@pytest.mark.parametrize("mode", ["tiled", "persistent", "auto"])
+def test_gpu_auto_order_is_the_models_choice(M, N, K, tile, mode):
+    from oracle import model as om
+
+    s = ts.Schedule(order="auto", mode=mode, tile=tile)
+    q = ts.query(M, N, K, s)
+    concurrent = min(q["cu_count"] * q["programs_per_cu"], q["grid"])
+    order, G, remap, pm = om.choose_order(q["num_m_tiles"], q["num_n_tiles"], q["grid"], concurrent, q["xcds"])
+    got = ("grouped" if q["order"] == 1 else "row_major", q["group_m"] if q["order"] == 1 else 1, bool(q["xcd_remap"]))
+    say(f"auto order {M}x{N}x{K} {tile} {mode}: {got}, model reuse {q['model_l2_reuse_pm']}")
+    assert got == (order, G, remap) and q["model_l2_reuse_pm"] == pm
+    resolved_mode = {0: "tiled", 1: "persistent", 2: "crosstile"}[q["mode"]]
+    resolved = ts.Schedule(order=order, group_m=G, mode=resolved_mode, xcd_remap=remap, tile=tile)
+    got_tr = ts.schedule_trace(M, N, K, s).numpy()
+    ref = _oracle(M, N, K, resolved, q["grid"])
+    assert np.array_equal(got_tr, ref)
+
+
+@pytest.mark.parametrize("M,N,K,tile", CASES)
+@pytest.mark.parametrize("mode", ["persistent", "crosstile", "streamk"])
+def test_gpu_trace_mulshift_equals_oracle(M, N, K, tile, mode):
+    s = ts.Schedule(order="grouped", group_m=8, mode=mode, xcd_remap=True, tile=tile, index_math="mulshift")
+    got = ts.schedule_trace(M, N, K, s).numpy()
+    ref = _oracle(M, N, K, s, ts.query(M, N, K, s)["grid"])
+    assert np.array_equal(got, ref)

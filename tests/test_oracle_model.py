@@ -134,3 +134,39 @@ def test_page_timings_are_2mnk_over_t():
                               ((4096, 4096, 4096), 0.6448, 213.16)]:
         assert m.flops(M, N, K) / (ms * 1e-3) / 1e12 == pytest.approx(tf, abs=0.02)
     assert math.isclose(1 - 10.4398 / 11.6640, 0.105, abs_tol=0.001)
+
+
+# ---- per-XCD L2 locality model -------------------------------------------------------------
+
+def test_l2_locality_hand_worked_4x4_grid_on_4_xcds():
+    # 4 x 4 tiles, 16 workgroups on 4 XCDs (4 tiles each), worked by hand:
+    # row-major: XCD x holds tile column x (4 rows + 1 column = 5 each, cost 20);
+    # row-major + remap: tile row x (cost 20); grouped G = 2 (with or without the
+    # remap): a 2 x 2 block per XCD (2 + 2 = 4 each, cost 16); G = 4 (column-major):
+    # cost 20 either way
+    L = m.l2_locality
+    assert L(4, 4, 16, 16, 4, "row_major", 1, False) == (20, 16)
+    assert L(4, 4, 16, 16, 4, "row_major", 1, True) == (20, 16)
+    assert L(4, 4, 16, 16, 4, "grouped", 2, False) == (16, 16)
+    assert L(4, 4, 16, 16, 4, "grouped", 2, True) == (16, 16)
+    assert L(4, 4, 16, 16, 4, "grouped", 4, False) == (20, 16)
+    assert L(4, 4, 16, 16, 4, "grouped", 4, True) == (20, 16)
+    # the choice: G = 8 and 16 are skipped (G > nm), G = 4 + remap costs 20, the
+    # first candidate of cost 16 is G = 2 + remap: reuse 1 - 16/32
+    assert m.choose_order(4, 4, 16, 16, 4) == ("grouped", 2, True, 500)
+
+
+@pytest.mark.parametrize("bm,concurrent,expect", [
+    # reuse fractions computed for the 16384 x 16384 grid when the build was planned
+    (256, 256, {("row_major", 1, False): 0.81, ("row_major", 1, True): 0.48, ("grouped", 4, False): 0.48,
+                ("grouped", 4, True): 0.81, ("grouped", 8, False): 0.48, ("grouped", 8, True): 0.81,
+                ("grouped", 16, False): 0.72, ("grouped", 16, True): 0.72}),
+    (128, 512, {("row_major", 1, False): 0.84, ("row_major", 1, True): 0.49, ("grouped", 4, False): 0.49,
+                ("grouped", 4, True): 0.84, ("grouped", 8, False): 0.49, ("grouped", 8, True): 0.88,
+                ("grouped", 16, False): 0.73, ("grouped", 16, True): 0.84}),
+])
+def test_l2_locality_planned_fractions_for_16384(bm, concurrent, expect):
+    nm = nn = 16384 // bm
+    for (order, G, remap), frac in expect.items():
+        cost, tiles = m.l2_locality(nm, nn, concurrent, concurrent, 8, order, G, remap)
+        assert round(1 - cost / (2 * tiles), 2) == frac, (order, G, remap)

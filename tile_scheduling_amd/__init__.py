@@ -30,14 +30,15 @@ _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 # status codes, element types and schedule enums (include/tsgemm.h)
 TS_OK, TS_ERR_INVALID_ARG, TS_ERR_UNSUPPORTED, TS_ERR_ALIGNMENT, TS_ERR_HIP, TS_ERR_NO_DEVICE = 0, -1, -2, -3, -4, -5
 TS_F16, TS_BF16, TS_F32 = 1, 2, 3
-ORDERS = {"row_major": 0, "grouped": 1}
-MODES = {"tiled": 0, "persistent": 1, "crosstile": 2, "streamk": 3}
+ORDERS = {"row_major": 0, "grouped": 1, "auto": 2}
+MODES = {"tiled": 0, "persistent": 1, "crosstile": 2, "streamk": 3, "auto": 4}
+INDEX_MATH = {"divide": 0, "mulshift": 1}
 TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3, "256x256x64w8": 4}
 
 
 class _Schedule(ctypes.Structure):
     _fields_ = [("order", _i32), ("group_m", _i32), ("mode", _i32),
-                ("num_programs", _i32), ("xcd_remap", _i32), ("tile_config", _i32)]
+                ("num_programs", _i32), ("xcd_remap", _i32), ("tile_config", _i32), ("index_math", _i32)]
 
 
 class LaunchInfo(ctypes.Structure):
@@ -47,7 +48,9 @@ class LaunchInfo(ctypes.Structure):
                 ("lds_bytes", _i32), ("masked", _i32), ("workspace_bytes", _i64), ("trace_items", _i64),
                 ("vgprs", _i32), ("scratch_bytes", _i32),
                 ("arch_vgprs", _i32), ("agprs", _i32), ("sgprs", _i32), ("spilled_vgprs", _i32),
-                ("spilled_sgprs", _i32), ("compiler_occupancy", _i32)]
+                ("spilled_sgprs", _i32), ("compiler_occupancy", _i32),
+                ("order", _i32), ("group_m", _i32), ("mode", _i32), ("xcd_remap", _i32), ("index_math", _i32),
+                ("model_l2_reuse_pm", _i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -93,22 +96,25 @@ def status_string(status: int) -> str:
 class Schedule:
     """Tile order and mode of one launch (see ts_schedule in include/tsgemm.h)."""
 
-    order: str = "row_major"      # "row_major" | "grouped"
+    order: str = "row_major"      # "row_major" | "grouped" | "auto"
     group_m: int = 8              # GROUP_SIZE_M for the grouped order
-    mode: str = "tiled"           # "tiled" | "persistent" | "crosstile" | "streamk"
+    mode: str = "tiled"           # "tiled" | "persistent" | "crosstile" | "streamk" | "auto"
     num_programs: int = 0         # persistent grid; 0 = CUs x workgroups per CU
     xcd_remap: bool = False       # contiguous tile-id runs per XCD
     tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64" | "256x256x64w8"
+    index_math: str = "divide"    # "divide" | "mulshift"
 
     def _c(self) -> _Schedule:
         return _Schedule(ORDERS[self.order], int(self.group_m), MODES[self.mode],
-                         int(self.num_programs), 1 if self.xcd_remap else 0, TILES[self.tile])
+                         int(self.num_programs), 1 if self.xcd_remap else 0, TILES[self.tile],
+                         INDEX_MATH[self.index_math])
 
     def label(self) -> str:
-        o = "rowmajor" if self.order == "row_major" else f"grouped{self.group_m}"
-        r = "+remap" if self.xcd_remap else ""
+        o = {"row_major": "rowmajor", "auto": "autoorder"}.get(self.order, f"grouped{self.group_m}")
+        r = "+remap" if self.xcd_remap and self.order != "auto" else ""
         p = f"/P{self.num_programs}" if self.mode != "tiled" and self.num_programs else ""
-        return f"{o}{r}/{self.mode}{p}/{self.tile}"
+        x = "/mulshift" if self.index_math == "mulshift" else ""
+        return f"{o}{r}/{self.mode}{p}/{self.tile}{x}"
 
 
 _TORCH_DTYPE = {torch.float16: TS_F16, torch.bfloat16: TS_BF16, torch.float32: TS_F32}

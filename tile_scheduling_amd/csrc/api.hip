@@ -8,7 +8,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "../../include/tsgemm.h"
 #include "internal.hpp"
@@ -83,6 +85,8 @@ ts_status current_device(int* dev_out, DeviceInfo* info) {
 }
 
 struct Plan {
+    bool auto_order;        // TS_ORDER_AUTO: order, G and remap chosen in resolve_grid
+    int l2_reuse_pm;        // the locality model's reuse of the resolved order (1/1000)
     int cfg;                // CFG_*
     int bm, bn, bk;
     int io;                 // IO_*
@@ -140,6 +144,62 @@ int choose_path(const Plan& p, int64_t N, int64_t K, uintptr_t a, uintptr_t b, i
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// TS_MODE_AUTO: the cross-tile loop for tiles of at most this many K steps.
+constexpr int64_t kCrossTileMaxSteps = 16;
+
+// Locality model of a schedule: the first `concurrent` workgroups of the launch
+// (the ones resident together; workgroup w runs on XCD w mod X) and the tiles they
+// start on.  Each XCD's L2 serves the A row panels and B column panels its tiles
+// share, so the cost is the number of distinct (XCD, tile row) plus (XCD, tile
+// column) pairs; the reuse fraction is 1 - cost / (2 x tiles).
+void locality_cost(const SchedArgs& s0, int concurrent, int64_t* cost, int64_t* tiles) {
+    SchedArgs s = s0;
+    s.fastdiv = 0;
+    std::vector<int64_t> rows, cols;
+    const int n = concurrent < s.grid ? concurrent : s.grid;
+    for (int w = 0; w < n; ++w) {
+        const int start = s.remap ? xcd_remap(w, s.grid, s.xcds) : w;
+        if (start >= s.num_tiles) continue;
+        int tm, tn;
+        tile_coords(s, start, tm, tn);
+        const int64_t x = w % s.xcds;
+        rows.push_back((x << 32) | tm);
+        cols.push_back((x << 32) | tn);
+    }
+    std::sort(rows.begin(), rows.end());
+    std::sort(cols.begin(), cols.end());
+    *tiles = (int64_t)rows.size();
+    *cost = (int64_t)(std::unique(rows.begin(), rows.end()) - rows.begin()) +
+            (int64_t)(std::unique(cols.begin(), cols.end()) - cols.begin());
+}
+
+// TS_ORDER_AUTO: the candidate of least locality cost, ties to the earlier one.
+void choose_order(SchedArgs* s, int concurrent, int* reuse_pm) {
+    struct Cand { int order, G, remap; };
+    static const Cand kCands[] = {{ORDER_GROUPED, 8, 1},  {ORDER_GROUPED, 4, 1},  {ORDER_GROUPED, 16, 1},
+                                  {ORDER_ROW_MAJOR, 1, 0}, {ORDER_ROW_MAJOR, 1, 1}, {ORDER_GROUPED, 8, 0},
+                                  {ORDER_GROUPED, 4, 0},  {ORDER_GROUPED, 16, 0}, {ORDER_GROUPED, 2, 1},
+                                  {ORDER_GROUPED, 32, 1}, {ORDER_GROUPED, 2, 0},  {ORDER_GROUPED, 32, 0}};
+    int64_t best_cost = -1, best_tiles = 0;
+    SchedArgs best = *s;
+    for (const Cand& c : kCands) {
+        if (c.order == ORDER_GROUPED && c.G > s->nm) continue;   // the same map as a smaller G
+        SchedArgs t = *s;
+        t.order = c.order;
+        t.group_m = c.G;
+        t.remap = c.remap;
+        int64_t cost, tiles;
+        locality_cost(t, concurrent, &cost, &tiles);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_tiles = tiles;
+            best = t;
+        }
+    }
+    *s = best;
+    *reuse_pm = best_tiles > 0 ? (int)(1000 - (1000 * best_cost) / (2 * best_tiles)) : 0;
+}
+
 // The compiler's resource report of a kernel, found through the symbol name of its
 // launch handle (the handle's symbol carries the kernel's mangled name).
 const KernelResources* resources_of(const void* fn) {
@@ -170,13 +230,15 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     else
         return TS_ERR_INVALID_ARG;
 
-    ts_schedule s = {TS_ORDER_ROW_MAJOR, 1, TS_MODE_TILED, 0, 0, TS_TILE_AUTO};
+    ts_schedule s = {TS_ORDER_ROW_MAJOR, 1, TS_MODE_TILED, 0, 0, TS_TILE_AUTO, TS_INDEX_DIVIDE};
     if (sp) s = *sp;
-    if (s.order != TS_ORDER_ROW_MAJOR && s.order != TS_ORDER_GROUPED) return TS_ERR_INVALID_ARG;
+    if (s.order != TS_ORDER_ROW_MAJOR && s.order != TS_ORDER_GROUPED && s.order != TS_ORDER_AUTO)
+        return TS_ERR_INVALID_ARG;
     if (s.order == TS_ORDER_GROUPED && s.group_m < 1) return TS_ERR_INVALID_ARG;
     if (s.mode != TS_MODE_TILED && s.mode != TS_MODE_PERSISTENT && s.mode != TS_MODE_CROSSTILE &&
-        s.mode != TS_MODE_STREAMK)
+        s.mode != TS_MODE_STREAMK && s.mode != TS_MODE_AUTO)
         return TS_ERR_INVALID_ARG;
+    if (s.index_math != TS_INDEX_DIVIDE && s.index_math != TS_INDEX_MULSHIFT) return TS_ERR_INVALID_ARG;
     if (s.num_programs < 0) return TS_ERR_INVALID_ARG;
     if (s.xcd_remap != 0 && s.xcd_remap != 1) return TS_ERR_INVALID_ARG;
     if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64_W8) return TS_ERR_INVALID_ARG;
@@ -195,17 +257,22 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     cfg_dims(cfg, &p->bm, &p->bn, &p->bk);
     const int64_t nm = cdiv64(M, p->bm), nn = cdiv64(N, p->bn), ks = cdiv64(K, p->bk);
     if (nm * nn > INT_MAX / 2 || ks > INT_MAX / 2) return TS_ERR_UNSUPPORTED;
+    if (s.mode == TS_MODE_AUTO)   // the merged loop pays where tiles are short (small K)
+        s.mode = (ks <= kCrossTileMaxSteps && cfg != CFG_256) ? TS_MODE_CROSSTILE : TS_MODE_PERSISTENT;
     p->mode = s.mode;
     p->requested_programs = s.num_programs;
     p->s.nm = (int)nm;
     p->s.nn = (int)nn;
     p->s.ks = (int)ks;
     p->s.num_tiles = (int)(nm * nn);
-    p->s.order = s.order;
+    p->auto_order = s.order == TS_ORDER_AUTO;
+    p->l2_reuse_pm = -1;
+    p->s.order = p->auto_order ? TS_ORDER_ROW_MAJOR : s.order;
     p->s.group_m = s.order == TS_ORDER_GROUPED ? (int)(s.group_m < nm ? s.group_m : (nm > 0 ? nm : 1)) : 1;
-    p->s.remap = s.xcd_remap;
+    p->s.remap = p->auto_order ? 0 : s.xcd_remap;
     p->s.xcds = 8;
     p->s.grid = 0;
+    p->s.fastdiv = s.index_math == TS_INDEX_MULSHIFT;
     // dense, 16-byte aligned operands assumed until ts_gemm sees the real ones
     const int64_t c_elem = c == TS_F32 ? 4 : 2;
     p->vec_a = (K % 8) == 0 ? 2 : (K % 2) == 0 ? 1 : 0;
@@ -257,6 +324,18 @@ ts_status resolve_grid(Plan* p, int cu_count, int ppc, int xcds) {
     } else {
         p->max_items = cdiv64(p->s.num_tiles, p->s.grid) * ksp;
     }
+    // workgroups resident together: the device's CUs x workgroups per CU (256 CUs
+    // and the plan's own grid when no device is known)
+    const int64_t resident = (cu_count > 0 && ppc > 0) ? (int64_t)cu_count * ppc : 256;
+    const int concurrent = (int)(resident < p->s.grid ? resident : p->s.grid);
+    if (p->auto_order) {
+        choose_order(&p->s, concurrent, &p->l2_reuse_pm);
+    } else {
+        int64_t cost, tiles;
+        locality_cost(p->s, concurrent, &cost, &tiles);
+        p->l2_reuse_pm = tiles > 0 ? (int)(1000 - (1000 * cost) / (2 * tiles)) : 0;
+    }
+    if (p->s.fastdiv) set_fastdiv(p->s);
     return TS_OK;
 }
 
@@ -350,7 +429,7 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     DeviceInfo di;
     st = current_device(&dev, &di);
     if (st != TS_OK) return st;
-    const int ppc = grid_needs_device ? programs_per_cu(p) : 1;
+    const int ppc = (grid_needs_device || p.auto_order) ? programs_per_cu(p) : 1;
     st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
     if (st != TS_OK) return st;
     if (clock_out && clock_rows < p.s.grid) return TS_ERR_INVALID_ARG;
@@ -471,6 +550,12 @@ extern "C" ts_status ts_query(int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
     out->masked = p.path;
     out->workspace_bytes = workspace_layout(p).total;
     out->trace_items = p.max_items;
+    out->order = p.s.order;
+    out->group_m = p.s.group_m;
+    out->mode = p.mode;
+    out->xcd_remap = p.s.remap;
+    out->index_math = p.s.fastdiv ? TS_INDEX_MULSHIFT : TS_INDEX_DIVIDE;
+    out->model_l2_reuse_pm = p.l2_reuse_pm;
     out->vgprs = -1;
     out->scratch_bytes = -1;
     const KernelResources* kr = resources_of(k.fn);
@@ -518,7 +603,7 @@ extern "C" ts_status ts_schedule_trace(int64_t M, int64_t N, int64_t K, int32_t 
     DeviceInfo di;
     st = current_device(&dev, &di);
     if (st != TS_OK) return st;
-    const int ppc = (p.mode != TS_MODE_TILED && p.requested_programs == 0) ? programs_per_cu(p) : 1;
+    const int ppc = ((p.mode != TS_MODE_TILED && p.requested_programs == 0) || p.auto_order) ? programs_per_cu(p) : 1;
     st = resolve_grid(&p, di.cu_count, ppc, di.xcds);
     if (st != TS_OK) return st;
     const int64_t need = (int64_t)p.s.grid * p.max_items;

@@ -41,6 +41,28 @@ namespace ts {
 enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
 enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2, MODE_STREAMK = 3 };
 
+// Division by an invariant divisor d >= 1 with one multiply-high, one add and one
+// shift, after Granlund and Montgomery, "Division by invariant integers using
+// multiplication" (PLDI 1994), with the round-up multiplier: for 0 <= n < 2^31,
+//   n / d = (umulhi(n, m) + n) >> l,  l = ceil(log2 d),  m = floor(2^32 (2^l - d) / d) + 1.
+// umulhi(n, m) <= n, so the sum stays below 2^32.  The multiplier is made on the
+// host once per launch.
+struct FastDiv {
+    uint32_t m;   // multiplier
+    uint32_t l;   // shift
+};
+
+TS_HD uint32_t umulhi32(uint32_t a, uint32_t b) { return (uint32_t)(((uint64_t)a * b) >> 32); }
+TS_HD int fdiv(int n, const FastDiv& f) { return (int)((umulhi32((uint32_t)n, f.m) + (uint32_t)n) >> f.l); }
+inline FastDiv make_fastdiv(int d) {
+    uint32_t l = 0;
+    while ((1ull << l) < (uint64_t)d) ++l;
+    FastDiv f;
+    f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - (uint64_t)d)) / (uint64_t)d + 1);
+    f.l = l;
+    return f;
+}
+
 // Everything a program needs to find its tiles.  Plain integers, passed by value
 // to kernels.  `group_m` is already clamped to [1, nm] by the host (values above
 // nm give the same map as nm and would only risk overflow in group_m * nn).
@@ -53,10 +75,25 @@ struct SchedArgs {
     int grid;          // programs launched (P, or num_tiles when tiled)
     int remap;         // XCD remap on/off
     int xcds;          // XCDs the dispatcher deals workgroups over
+    int fastdiv;       // 1: tile_coords divides by the multipliers below
+    FastDiv f_nn;      // by nn
+    FastDiv f_group;   // by G * nn (tiles per band)
+    FastDiv f_g;       // by G (rows of a full band)
+    FastDiv f_glast;   // by the rows of the last band
 };
 
 TS_HD int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 TS_HD int min_i(int a, int b) { return a < b ? a : b; }
+
+// Fills the multipliers of s (nm, nn and group_m set); used when s.fastdiv is on.
+inline void set_fastdiv(SchedArgs& s) {
+    const int G = s.group_m > 0 ? s.group_m : 1;
+    s.f_nn = make_fastdiv(s.nn > 0 ? s.nn : 1);
+    s.f_group = make_fastdiv(G * (s.nn > 0 ? s.nn : 1));
+    s.f_g = make_fastdiv(G);
+    const int last_rows = s.nm > 0 ? s.nm - ((s.nm - 1) / G) * G : 1;
+    s.f_glast = make_fastdiv(last_rows);
+}
 
 TS_HD int xcd_remap(int w, int n, int X) {
     const int q = n / X, r = n % X, x = w % X;
@@ -69,6 +106,20 @@ TS_HD int xcd_remap(int w, int n, int X) {
 TS_HD void tile_coords(const SchedArgs& s, int t, int& tm, int& tn) {
     if (t >= s.num_tiles) {
         tm = tn = 0;
+    } else if (s.fastdiv) {   // the same map, divisions by multiply-high
+        if (s.order == ORDER_GROUPED) {
+            const int gid = fdiv(t, s.f_group);
+            const int tig = t - gid * (s.group_m * s.nn);
+            const int first_m = gid * s.group_m;
+            const bool full = first_m + s.group_m <= s.nm;
+            const int gs = full ? s.group_m : s.nm - first_m;
+            const int q = fdiv(tig, full ? s.f_g : s.f_glast);
+            tm = first_m + (tig - q * gs);
+            tn = q;
+        } else {
+            tm = fdiv(t, s.f_nn);
+            tn = t - tm * s.nn;
+        }
     } else if (s.order == ORDER_GROUPED) {
         const int in_group = s.group_m * s.nn;            // tiles per full group
         const int gid = t / in_group;
