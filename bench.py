@@ -416,6 +416,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_16384x16384x4096_f16")
+    ap.add_argument("--layout", default="NN", choices=["NN", "NT", "TN", "TT"],
+                    help="operand storage: A [M][K] (N) or [K][M] (T), B [K][N] (N) or [N][K] (T)")
     ap.add_argument("--schedule", default=DEFAULT_SCHEDULE)
     ap.add_argument("--sweep", action="store_true", help="also time every schedule (table on stderr)")
     ap.add_argument("--ksweep", action="store_true",
@@ -463,8 +465,14 @@ def main():
     in_dtype = torch.float16 if w.ab_dtype == "f16" else torch.bfloat16
 
     A, B = workloads.inputs(w)
-    a = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
-    b = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
+    if args.layout[0] == "T":   # A stored [K][M]: the same values through a transposed view
+        a = torch.from_numpy(np.ascontiguousarray(A.T).view(np.int16)).view(in_dtype).cuda().t()
+    else:
+        a = torch.from_numpy(A.view(np.int16)).view(in_dtype).cuda()
+    if args.layout[1] == "T":   # B stored [N][K]
+        b = torch.from_numpy(np.ascontiguousarray(B.T).view(np.int16)).view(in_dtype).cuda().t()
+    else:
+        b = torch.from_numpy(B.view(np.int16)).view(in_dtype).cuda()
     c = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda")
     flops = 2.0 * w.M * w.N * w.K
 
@@ -539,7 +547,8 @@ def main():
         "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.ab_dtype, "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.ab_dtype, "acc": "f32",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": args.layout, "in": w.ab_dtype,
+                   "acc": "f32",
                    "out": w.c_dtype, "inputs": f"{w.dist} seed {w.seed}", "schedule": sched.label(),
                    "resolved_schedule": resolved_label(q),
                    "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "threads": q["threads"],

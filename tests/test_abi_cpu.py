@@ -45,7 +45,10 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below is rejec
     (dict(ab=ts.TS_F16, c=ts.TS_BF16), ts.TS_ERR_UNSUPPORTED),
     (dict(ab=ts.TS_F32, c=ts.TS_F32), ts.TS_ERR_UNSUPPORTED),
     (dict(ab=9), ts.TS_ERR_INVALID_ARG),
-    (dict(strides=(64, 2, 64, 1, 64, 1)), ts.TS_ERR_UNSUPPORTED),
+    (dict(strides=(64, 2, 64, 1, 64, 1)), ts.TS_ERR_UNSUPPORTED),      # neither A stride is 1
+    (dict(strides=(64, 1, 64, 2, 64, 1)), ts.TS_ERR_UNSUPPORTED),      # neither B stride is 1
+    (dict(strides=(1, 10, 64, 1, 64, 1)), ts.TS_ERR_INVALID_ARG),      # A stored [K][M] with stride < M
+    (dict(strides=(64, 1, 1, 10, 64, 1)), ts.TS_ERR_INVALID_ARG),      # B stored [N][K] with stride < K
     (dict(strides=(64, 1, 64, 1, 64, 3)), ts.TS_ERR_UNSUPPORTED),
     (dict(strides=(10, 1, 64, 1, 64, 1)), ts.TS_ERR_INVALID_ARG),   # lda < K
     (dict(strides=(64, 1, 64, 1, 10, 1)), ts.TS_ERR_INVALID_ARG),   # ldc < N
@@ -266,3 +269,11 @@ def test_mulshift_index_math_gives_the_same_map(order, G, M, N):
                         index_math="mulshift")
         assert ts.query(M, N, 256, b)["index_math"] == 1
         assert np.array_equal(ts.schedule_trace_host(M, N, 256, a), ts.schedule_trace_host(M, N, 256, b))
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+@pytest.mark.parametrize("strides", [(64, 1, 64, 1, 64, 1), (64, 1, 1, 64, 64, 1), (1, 64, 64, 1, 64, 1),
+                                     (1, 64, 1, 64, 64, 1)], ids=["NN", "NT", "TN", "TT"])
+def test_four_layouts_pass_validation(strides):
+    # valid: rejected only because there is no device
+    assert ts.gemm_raw(FAKE, FAKE, FAKE, 64, 64, 64, strides=strides) == ts.TS_ERR_NO_DEVICE

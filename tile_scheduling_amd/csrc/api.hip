@@ -387,29 +387,48 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     if (st != TS_OK) return st;
     if (M == 0 || N == 0) return TS_OK;
     if (!C || (K > 0 && (!A || !B))) return TS_ERR_INVALID_ARG;
-    if (stride_ak != 1 || stride_bn != 1 || stride_cn != 1) return TS_ERR_UNSUPPORTED;
-    if ((M > 1 && K > 0 && stride_am < K) || (K > 1 && stride_bk < N) || (M > 1 && stride_cm < N))
+    // Operand layouts: A stored [M][K] (stride_ak == 1) or [K][M] (stride_am == 1);
+    // B stored [K][N] (stride_bn == 1) or [N][K] (stride_bk == 1); C stored [M][N].
+    // A dimension of extent 1 makes its stride irrelevant: it is read as unit.
+    if (M <= 1) stride_am = stride_ak == 1 ? stride_am : 1;
+    if (K <= 1) { stride_ak = 1; stride_bk = stride_bn == 1 ? (stride_bk > N ? stride_bk : N) : 1; }
+    if (N <= 1) stride_bn = stride_bk == 1 ? stride_bn : 1;
+    if (stride_am < 0 || stride_ak < 0 || stride_bk < 0 || stride_bn < 0 || stride_cm < 0) return TS_ERR_INVALID_ARG;
+    if (stride_cn != 1) return TS_ERR_UNSUPPORTED;
+    const bool a_kmaj = stride_ak == 1, b_nmaj = stride_bn == 1;
+    if (!(a_kmaj || stride_am == 1) || !(b_nmaj || stride_bk == 1)) return TS_ERR_UNSUPPORTED;
+    const int64_t lda = a_kmaj ? stride_am : stride_ak;    // distance between stored rows
+    const int64_t ldb = b_nmaj ? stride_bk : stride_bn;
+    if ((a_kmaj && M > 1 && K > 0 && lda < K) || (!a_kmaj && K > 1 && lda < M) ||
+        (b_nmaj && K > 1 && ldb < N) || (!b_nmaj && N > 1 && K > 0 && ldb < K) || (M > 1 && stride_cm < N))
         return TS_ERR_INVALID_ARG;
-    if (stride_am < 0 || stride_bk < 0 || stride_cm < 0) return TS_ERR_INVALID_ARG;
-    if (stride_am > INT_MAX || stride_bk > INT_MAX || stride_cm > INT_MAX) return TS_ERR_UNSUPPORTED;
+    if (lda > INT_MAX || ldb > INT_MAX || stride_cm > INT_MAX) return TS_ERR_UNSUPPORTED;
     const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
     const int c_elem = c_dtype == TS_F32 ? 4 : 2;
     if ((a & 1) || (b & 1) || (c % c_elem)) return TS_ERR_ALIGNMENT;
 
     // Alignment levels of the rows: 16-byte operand vectors need 16-byte aligned
     // rows, 4-byte pieces 4-byte aligned ones; C vectors are 4 elements, pieces 2.
-    p.vec_a = (a % 16 == 0) && (stride_am % 8 == 0 || M == 1) ? 2
-              : (a % 4 == 0) && (stride_am % 2 == 0 || M == 1) ? 1 : 0;
-    p.vec_b = (b % 16 == 0) && (stride_bk % 8 == 0 || K <= 1) ? 2
-              : (b % 4 == 0) && (stride_bk % 2 == 0 || K <= 1) ? 1 : 0;
+    // A stored [K][M] is gathered element by element (level 0 for its vectors).
+    p.vec_a = !a_kmaj ? 0 : (a % 16 == 0) && (lda % 8 == 0 || M == 1) ? 2
+              : (a % 4 == 0) && (lda % 2 == 0 || M == 1) ? 1 : 0;
+    p.vec_b = (b % 16 == 0) && (ldb % 8 == 0 || (b_nmaj ? K <= 1 : N <= 1)) ? 2
+              : (b % 4 == 0) && (ldb % 2 == 0 || (b_nmaj ? K <= 1 : N <= 1)) ? 1 : 0;
     p.vec_c = (c % (4 * c_elem) == 0) && (stride_cm % 4 == 0 || M == 1) ? 2
               : (c % (2 * c_elem) == 0) && (stride_cm % 2 == 0 || M == 1) ? 1 : 0;
     p.masked = (M % p.bm) != 0 || (N % p.bn) != 0 || (K % p.bk) != 0 || K == 0 || p.vec_a != 2 ||
                p.vec_b != 2 || p.vec_c != 2;
     // The unmasked kernels form row offsets inside a tile as 32-bit byte counts; the
     // masked ones use full-width pointers.
-    if ((int64_t)p.bm * stride_am * 2 > INT_MAX || (int64_t)p.bk * stride_bk * 2 > INT_MAX) p.masked = 1;
-    p.path = choose_path(p, N, K, a, b, stride_am, stride_bk);
+    if ((int64_t)p.bm * lda * 2 > INT_MAX || (int64_t)(b_nmaj ? p.bk : p.bn) * ldb * 2 > INT_MAX) p.masked = 1;
+    if (a_kmaj && b_nmaj) {
+        p.path = choose_path(p, N, K, a, b, lda, ldb);
+    } else if (a_kmaj && !p.masked && cfg_has_fast_path(p.cfg)) {
+        p.path = PATH_FULL_BT;   // whole tiles, B stored [N][K] (its rows 16-byte aligned)
+    } else {
+        p.path = PATH_MASKED;    // A stored [K][M], or ragged / unaligned with B stored [N][K]
+        p.masked = true;
+    }
 
     auto workspace_check = [&](const Plan& q) -> ts_status {
         const WorkspaceLayout w = workspace_layout(q);
@@ -454,9 +473,13 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     g.M = (int)M;
     g.N = (int)N;
     g.K = (int)K;
-    g.lda = stride_am;
-    g.ldb = stride_bk;
+    g.lda = lda;
+    g.ldb = ldb;
     g.ldc = stride_cm;
+    g.sam = stride_am;
+    g.sak = stride_ak;
+    g.sbk = stride_bk;
+    g.sbn = stride_bn;
     g.vec_a = p.vec_a;
     g.vec_b = p.vec_b;
     g.vec_c = p.vec_c;
@@ -466,8 +489,8 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
         while (ca > 2 && ((c % ca) != 0 || (M > 1 && pitch % ca != 0))) ca >>= 1;
         g.c_align = ca;
     }
-    g.a_bytes = K > 0 ? ((M - 1) * stride_am + K) * 2 : 0;
-    g.b_bytes = K > 0 ? ((K - 1) * stride_bk + N) * 2 : 0;
+    g.a_bytes = K > 0 ? ((M - 1) * stride_am + (K - 1) * stride_ak + 1) * 2 : 0;
+    g.b_bytes = K > 0 ? ((K - 1) * stride_bk + (N - 1) * stride_bn + 1) * 2 : 0;
     g.s = p.s;
     g.clk = reinterpret_cast<unsigned long long*>(clock_out);
     g.sk_flags = wl.total > 0 ? static_cast<int*>(workspace) : nullptr;

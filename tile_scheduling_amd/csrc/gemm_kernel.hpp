@@ -67,7 +67,10 @@ struct GemmArgs {
     const uint16_t* B;
     void* C;
     int M, N, K;
-    long long lda, ldb, ldc;  // row strides in elements (inner strides are 1)
+    long long lda, ldb, ldc;  // strides between the stored rows, in elements: A [M][K] (lda = stride_am),
+                              // B [K][N] (ldb = stride_bk) or, on PATH_FULL_BT, B stored [N][K] (ldb =
+                              // stride_bn); C [M][N]
+    long long sam, sak, sbk, sbn;  // all four element strides (the masked path gathers with them)
     // Row alignment of A, B (16-bit elements) and C: 2 if rows allow 16-byte (A, B) /
     // full 4-element (C) vectors, 1 if they allow 4-byte (A, B) / 2-element (C) pieces,
     // 0 if only single elements.
@@ -210,6 +213,15 @@ template <> struct Out<OutBF16> {
     }
 };
 
+// 16-bit elements p[0], p[stride], ..., p[7 stride], those at or past `valid` read
+// as zero, packed as 8 consecutive values (a strided operand on the masked path).
+__device__ __forceinline__ u32x4 gather8_masked(const uint16_t* p, long long stride, int valid) {
+    uint32_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = (q < valid) ? (uint32_t)p[q * stride] : 0u;
+    return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
 // 8 consecutive 16-bit elements p[0..7], those at or past `valid` read as zero.
 // `vec` is the alignment level of p (2: 16 bytes, 1: 4 bytes, 0: 2 bytes).
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t* p, int valid, int vec) {
@@ -278,14 +290,17 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 //  register (other masked shapes, or BK = 32): A and B one slice ahead in registers,
 //    written at the last sub-steps into the other slot of two; B is transposed to
 //    [n][k] with byte permutes on the way in.
-// Kernel paths: whole tiles; masked register pipeline; direct-to-LDS pipeline with
-// ragged edges zero-filled by the loads' range checks.
-enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE = 2 };
+// Kernel paths: whole tiles; masked register pipeline (any operand layout); direct-
+// to-LDS pipeline with ragged edges zero-filled by the loads' range checks; whole
+// tiles with B stored [N][K] (K contiguous, as A), whose B slices are staged and read
+// exactly as A's.
+enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE = 2, PATH_FULL_BT = 3 };
 
 template <class Cfg, class TI, class TO, int PATH>
 struct Engine {
     static constexpr bool MASKED = PATH == PATH_MASKED;
     static constexpr bool EDGE = PATH == PATH_EDGE;
+    static constexpr bool BT = PATH == PATH_FULL_BT;   // B stored [N][K]
     static constexpr bool EDGES = PATH != PATH_FULL;   // C stores masked to M x N
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH, SUB = Cfg::SUB;
@@ -305,7 +320,9 @@ struct Engine {
     static_assert(!EDGE || FAST, "the edge paths run the direct-to-LDS pipeline");
     static constexpr int BH = RBB / 256;                                // 256-byte pieces of a B row
     static constexpr int A_DMA_N = FAST ? BM * RB / 1024 / NW : 0;   // 1 KiB A loads per wave
-    static constexpr int B_DMA_N = FAST ? BK * RBB / 1024 / NW : 0;  // 1 KiB B loads per wave
+    static constexpr int B_DMA_N = !FAST ? 0 : BT ? BN * RB / 1024 / NW   // 1 KiB B loads per wave
+                                                  : BK * RBB / 1024 / NW;
+    static_assert(!BT || FAST, "B stored [N][K] runs on the direct-to-LDS pipeline");
     static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
     static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
     static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
@@ -331,6 +348,7 @@ struct Engine {
     uint32_t b_sel[2];    // register path: byte-permute selector of B writes with even / odd j
     // per-lane global byte offsets
     uint32_t a_go[2], b_go;   // A: [c&1] of the load / chunk index c
+    uint32_t bt_go[2];        // PATH_FULL_BT: B's load offsets, as a_go
     uint32_t a_kc[2];         // edge paths: first k (element) of the A chunk a_go[e] points at
     int klim = 0;             // edge paths: k elements of the A slice being loaded that exist
     bool b_active;        // this thread owns a B loader block
@@ -375,6 +393,8 @@ struct Engine {
                 a_go[e] = (uint32_t)(((long long)row * g.lda + ((pc ^ row ^ grp7) * 8)) * 2);
                 a_kc[e] = (uint32_t)((pc ^ row ^ grp7) * 8);
                 a_wr[e] = 0;
+                // B stored [N][K]: its [n][k] slot is filled exactly as A's [m][k] slot
+                bt_go[e] = (uint32_t)(((long long)row * g.ldb + ((pc ^ row ^ grp7) * 8)) * 2);
             }
             // B: [k][n] rows whose 16-byte chunks are XOR-swizzled by
             //   f(k) = 4 (k mod 4) ^ 2 (bit 3 of k),
@@ -452,9 +472,9 @@ struct Engine {
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             asm volatile("" : "+v"(a_rd[s]));
-            if (!FAST) asm volatile("" : "+v"(b_rd[s]));
+            if (!FAST || BT) asm volatile("" : "+v"(b_rd[s]));
         }
-        if (FAST) {
+        if (FAST && !BT) {
 #pragma unroll
             for (int u = 0; u < NJB; ++u) asm volatile("" : "+v"(bt_rd[u]));
         } else {
@@ -556,8 +576,18 @@ struct Engine {
     // buffer load is made per dword (both checked on MI355X with an in-bounds probe),
     // so a load that straddles the end of B returns its dwords before the end and
     // zeros after it.
+    // Element offset of B's slice k of tile column n0 (the slice's first element).
+    __device__ __forceinline__ long long b_slice(int n0, int k) const {
+        return BT ? (long long)n0 * g.ldb + k * BK : (long long)k * BK * g.ldb + n0;
+    }
     template <int SLOT>
     __device__ __forceinline__ void dma_b_one(int c, const __amdgpu_buffer_rsrc_t& r) {
+        if constexpr (BT) {   // as dma_a_one, over B's [n][k] rows
+            const int grp = c * NW + wave;
+            const int e = ((c * NW) >> 2) & 1;
+            dma16(r, bt_go[e], (int)((long long)grp * 8 * g.ldb * 2), lb[SLOT] + grp * 1024);
+            return;
+        }
         const int grp = c * NW + wave;                 // RPD-row group (1 KiB)
         const int e = ((c * NW * RPD) >> 3) & 1;
         if constexpr (EDGE)
@@ -567,7 +597,7 @@ struct Engine {
     }
     template <int SLOT>
     __device__ __forceinline__ void dma_b(int n0, int k, int valid) {
-        const __amdgpu_buffer_rsrc_t r = rsrc_b((long long)k * BK * g.ldb + n0, valid);
+        const __amdgpu_buffer_rsrc_t r = rsrc_b(b_slice(n0, k), valid);
 #pragma unroll
         for (int c = 0; c < B_DMA_N; ++c) dma_b_one<SLOT>(c, r);
     }
@@ -589,9 +619,13 @@ struct Engine {
             const int idx = c * NT + tid;
             const int row = idx / KCH, kc = idx % KCH;
             const int gm = m0 + row, gk = k0 + kc * 8;
-            const uint16_t* p = g.A + (long long)gm * g.lda + gk;
             const bool in = valid && (Cfg::NA % NT == 0 || idx < Cfg::NA) && gm < g.M;
-            ra[c] = in ? load8_masked(p, g.K - gk, g.vec_a) : u32x4{0, 0, 0, 0};
+            if (!in)
+                ra[c] = u32x4{0, 0, 0, 0};
+            else if (g.sak == 1)
+                ra[c] = load8_masked(g.A + (long long)gm * g.lda + gk, g.K - gk, g.vec_a);
+            else   // A stored [K][M]: 8 consecutive k of row gm, g.sak apart
+                ra[c] = gather8_masked(g.A + (long long)gm * g.sam + (long long)gk * g.sak, g.sak, g.K - gk);
         }
     }
 
@@ -618,9 +652,13 @@ struct Engine {
         const int gn = n0 + nb * 8, gk = k0 + kb * KBH;
 #pragma unroll
         for (int q = 0; q < KBH; ++q) {
-            const uint16_t* p = g.B + (long long)(gk + q) * g.ldb + gn;
-            rb[SET][q] = (valid && b_active && gk + q < g.K) ? load8_masked(p, g.N - gn, g.vec_b)
-                                                            : u32x4{0, 0, 0, 0};
+            if (!(valid && b_active && gk + q < g.K))
+                rb[SET][q] = u32x4{0, 0, 0, 0};
+            else if (g.sbn == 1)
+                rb[SET][q] = load8_masked(g.B + (long long)(gk + q) * g.ldb + gn, g.N - gn, g.vec_b);
+            else   // B stored [N][K]: 8 consecutive n of row gk + q, g.sbn apart
+                rb[SET][q] = gather8_masked(g.B + (long long)(gk + q) * g.sbk + (long long)gn * g.sbn, g.sbn,
+                                            g.N - gn);
         }
     }
 
@@ -680,7 +718,7 @@ struct Engine {
     // B fragment of 32-column block j at sub-step s from slot SLOT.
     template <int SLOT>
     __device__ __forceinline__ u32x4 read_b(int s, int j) const {
-        if (FAST) {   // two transpose reads: k offsets 0-3 and 4-7 of the lane's half
+        if (FAST && !BT) {   // two transpose reads: k offsets 0-3 and 4-7 of the lane's half
             const char* base = lb[SLOT] + (j >> 2) * 256 + 16 * s * RBB;
             const u32x2 lo = lds_read_tr(base, bt_rd[j & 3]);
             const u32x2 hi = lds_read_tr(base + 4 * RBB, bt_rd[j & 3]);
@@ -876,7 +914,7 @@ struct Engine {
     template <int SLOT>
     __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false) {
         if constexpr (FAST) {
-            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b((long long)nx.kb * BK * g.ldb + nx.n0, nx.vb);
+            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_slice(nx.n0, nx.kb), nx.vb);
             const __amdgpu_buffer_rsrc_t ra_ = rsrc_a((long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
             if constexpr (EDGE) klim = g.K - nx.ka * BK;
             fast_sub<SLOT, 0>(ra_, rb_);

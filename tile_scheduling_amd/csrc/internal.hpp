@@ -51,8 +51,14 @@ const void* kernel_by_mode(int mode) {
 // configurations compile in parallel in halves.
 template <class Cfg, class TI, class TO>
 const void* kernel_by_path_base(int path, int mode) {
-    return path == PATH_FULL ? kernel_by_mode<Cfg, TI, TO, PATH_FULL>(mode)
-                             : kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
+    if (path == PATH_FULL) return kernel_by_mode<Cfg, TI, TO, PATH_FULL>(mode);
+    if (path == PATH_FULL_BT) {
+        if constexpr (Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK)
+            return kernel_by_mode<Cfg, TI, TO, PATH_FULL_BT>(mode);
+        else
+            return nullptr;
+    }
+    return kernel_by_mode<Cfg, TI, TO, PATH_MASKED>(mode);
 }
 template <class Cfg, class TI, class TO>
 const void* kernel_by_path_edge(int path, int mode) {
@@ -86,7 +92,7 @@ template <class Cfg>
 constexpr bool has_fast_path() { return Engine<Cfg, InF16, OutF16, PATH_FULL>::FAST_OK; }
 
 // One function per tile configuration, each defined in its own translation unit.
-// path PATH_FULL or PATH_MASKED
+// path PATH_FULL, PATH_FULL_BT or PATH_MASKED
 KernelRef kernels_cfg64(int io, int path, int mode);
 KernelRef kernels_cfg128(int io, int path, int mode);
 KernelRef kernels_cfg256(int io, int path, int mode);
