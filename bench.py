@@ -10,7 +10,7 @@ last hardware-counter profile measured for this kernel source, and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--schedule S] [--workload NAME]
-                    [--sweep] [--ksweep] [--extras] [--pps-sweep] [--index-ablation]
+                    [--sweep] [--ksweep] [--extras] [--pps-sweep] [--index-ablation] [--pingpong-ab]
                     [--pmc-target | --stall-target | --target mix|ksweep|ragged]
 
 --sweep times every order x remap x mode at the workload; --ksweep times the
@@ -19,7 +19,9 @@ at 16384 x 16384; --extras times the benchmarked launch hot and cold, the 8192
 grid, the ragged bf16 workload and one GPU's share of an eight-way row split,
 and the oracle on one host thread (tables on stderr, before the JSON line).
 --pps-sweep times one and two workgroups per CU for the 128x128x64 tile;
---index-ablation times the tile-order maps by division against multiply-shift.
+--index-ablation times the tile-order maps by division against multiply-shift;
+--pingpong-ab times the ping-pong kernel against the 8-wave kernel and runs the
+barrier-phase probe.
 --pmc-target, --stall-target and --target only run the fixed launch sequences
 that the hardware-counter passes profile.
 
@@ -331,6 +333,32 @@ def index_ablation(ts, torch, np, workloads, steps):
         del a, b, c
 
 
+def pingpong_ab(ts, torch, np, workloads, steps):
+    """The ping-pong kernel against the 8-wave kernel of the same tile, launches
+    interleaved per workload, and the barrier-phase probe (stderr table)."""
+    for pat, what in ((0, "no barrier"), (1, "barrier every 8 MFMAs, all waves"),
+                      (2, "ping-pong, 16-MFMA phases"), (3, "ping-pong, 32-MFMA phases")):
+        log(f"phase-probe pattern {pat} ({what}): {ts.mfma_phase_tflops(pat):8.1f} TFLOP/s")
+    names = ["gemm_16384x16384x4096_f16", "gemm_8192x8192x4096_f16", "gemm_16384x16384x4096_bf16",
+             "gemm_16384x16384x128_f16_ksweep", "gemm_16384x16384x1024_f16_ksweep", "gemm_5000x12290x1000_bf16_f32"]
+    by = {x.name: x for x in workloads.ALL}
+    for wname in names:
+        w = by[wname]
+        a, b, c = _device_inputs(ts, torch, np, w)
+        flops = 2.0 * w.M * w.N * w.K
+        for mode in ("persistent", "crosstile"):
+            labs = [f"grouped8+remap/{mode}/256x256x64w8", f"grouped8+remap/{mode}/256x256x64pp"]
+            res = {lab: [] for lab in labs}
+            for _ in range(3):   # interleaved, so that both see the same clock drift
+                for lab in labs:
+                    res[lab].append(time_gemm(ts, torch, a, b, c, parse_schedule(lab), steps, 10)["median_ms"])
+            for lab in labs:
+                ms = sorted(res[lab])[1]
+                log(f"pingpong {wname} {lab:40s} median of 3 medians {ms:.4f} ms  "
+                    f"{flops / ms / 1e9:8.1f} TFLOP/s")
+        del a, b, c
+
+
 KSWEEP_SCHEDULES = ("grouped8+remap/persistent", "grouped8+remap/crosstile")
 
 
@@ -437,6 +465,9 @@ def main():
                     help="also time programs per CU 1 and 2 for the 128x128x64 tile (stderr table)")
     ap.add_argument("--index-ablation", action="store_true",
                     help="also time the tile maps by integer division against multiply-shift (stderr table)")
+    ap.add_argument("--pingpong-ab", action="store_true",
+                    help="also time the ping-pong kernel against the 8-wave kernel and run the "
+                         "barrier-phase probe (stderr table)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -482,6 +513,8 @@ def main():
         pps_sweep(ts, torch, np, workloads, max(10, args.steps))
     if args.index_ablation:
         index_ablation(ts, torch, np, workloads, max(10, args.steps))
+    if args.pingpong_ab:
+        pingpong_ab(ts, torch, np, workloads, max(10, args.steps))
     if args.extras:
         extras(ts, torch, np, workloads, a, b, c, w, parse_schedule(args.schedule), max(10, args.steps))
     if args.sweep:

@@ -111,7 +111,14 @@ enum {
     TS_TILE_128x128x64 = 2,
     TS_TILE_256x256x64 = 3,    /* 4 waves of 128x128 (one per SIMD); tiled and persistent
                                   modes only (TS_MODE_CROSSTILE: TS_ERR_UNSUPPORTED) */
-    TS_TILE_256x256x64_W8 = 4  /* 8 waves of 128x64 (two per SIMD)   */
+    TS_TILE_256x256x64_W8 = 4, /* 8 waves of 128x64 (two per SIMD)   */
+    TS_TILE_256x256x64_PP = 5  /* the _W8 tile and wave layout run as two groups of four
+                                  waves that take turns: in each phase of a K step one
+                                  group multiplies while the other reads its next
+                                  fragments from LDS.  Each program's tiles form one
+                                  stream of (tile, K step) items, so the tile boundary
+                                  does not drain the pipeline in any mode.  Stream-K and
+                                  the masked register path run the _W8 kernels.       */
 };
 
 typedef struct {
@@ -280,6 +287,23 @@ ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
  * TS_ERR_NO_DEVICE, TS_ERR_HIP (launch failure).
  */
 ts_status ts_mfma_loop_probe(int32_t iters, float* sink, int64_t sink_elems, double* flops, void* stream);
+
+/* ts_mfma_phase_probe: the probe above with its MFMA stream cut by workgroup barriers,
+ * the cost of a barrier pattern on its own (no memory traffic).  This library's own
+ * measurement addition, for the choice between one barrier per K half-step and the
+ * ping-pong kernel's alternating phases.  Per iteration every wave issues 16 MFMAs
+ * (pattern 3: 32):
+ *   0  no barrier;
+ *   1  every wave: 8 MFMAs, barrier, 8 MFMAs, barrier;
+ *   2  ping-pong: waves 0-3 issue 16 MFMAs while waves 4-7 wait at a barrier, then the
+ *      other way round;
+ *   3  ping-pong with 32-MFMA phases.
+ * Operands are the same constants as the loop probe's.  `sink` as there; `flops`
+ * receives the launch's FLOPs.  Errors: TS_ERR_INVALID_ARG (iters <= 0, pattern
+ * outside 0..3, null or short sink, null flops), TS_ERR_NO_DEVICE, TS_ERR_HIP.
+ * Asynchronous on `stream`. */
+ts_status ts_mfma_phase_probe(int32_t iters, int32_t pattern, float* sink, int64_t sink_elems, double* flops,
+                              void* stream);
 
 /*
  * This library's own addition (the pages print no such trace): writes the work

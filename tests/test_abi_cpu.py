@@ -71,7 +71,7 @@ def test_invalid_arguments_are_rejected(kw, expect):
 def test_bad_schedule_enums_are_rejected():
     s = ts._Schedule(5, 1, 0, 0, 0, 0)
     assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(s), None) == -1
-    for bad in (ts._Schedule(0, 1, 5, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 9),
+    for bad in (ts._Schedule(0, 1, 5, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 2, 0), ts._Schedule(0, 1, 0, 0, 0, 6),
                 ts._Schedule(3, 1, 0, 0, 0, 0), ts._Schedule(0, 1, 0, 0, 0, 0, 2)):
         assert ts._lib.ts_gemm(FAKE, FAKE, FAKE, 64, 64, 64, 64, 1, 64, 1, 64, 1, 1, 1, ctypes.byref(bad), None) == -1
 
@@ -111,6 +111,17 @@ def test_query_tile_grid_and_masking():
     assert q["k_steps"] == 0 and q["masked"] == 1  # K = 0 still writes C (zeros)
 
 
+def test_pingpong_tile_has_the_8_wave_tiles_geometry():
+    # same tile, threads and LDS as the 8-wave configuration; stream-K and the masked
+    # register path run the 8-wave kernels
+    for M, N, K, mode in [(16384, 16384, 4096, "persistent"), (5000, 12290, 1000, "crosstile"),
+                          (1000, 1001, 77, "persistent"), (5000, 12290, 1000, "streamk")]:
+        qs = [ts.query(M, N, K, ts.Schedule(order="grouped", group_m=8, mode=mode, num_programs=256, tile=t))
+              for t in ("256x256x64w8", "256x256x64pp")]
+        for key in ("block_m", "block_n", "block_k", "grid", "threads", "lds_bytes", "masked", "workspace_bytes"):
+            assert qs[0][key] == qs[1][key], key
+
+
 def test_four_wave_256_tile_has_no_crosstile_kernel():
     s = ts.Schedule(mode="crosstile", num_programs=8, tile="256x256x64")
     with pytest.raises(ts.TsError) as e:
@@ -121,7 +132,7 @@ def test_four_wave_256_tile_has_no_crosstile_kernel():
         ts.query(1024, 1024, 512, ts.Schedule(mode=mode, num_programs=8, tile="256x256x64"))
 
 
-@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8", "256x256x64pp"])
 @pytest.mark.parametrize("M,N,K", [(16384, 16384, 4096), (5000, 12290, 1000), (333, 290, 150)])
 @pytest.mark.parametrize("mode", ["tiled", "persistent", "crosstile"])
 def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
@@ -156,6 +167,7 @@ CASES = [
     (5000, 12290, 1000, "256x256x64w8"),
     (2048, 3072, 0, "256x256x64w8"),
     (64, 64, 33, "64x64x32"),
+    (5000, 12290, 1000, "256x256x64pp"),
 ]
 
 
@@ -167,7 +179,7 @@ CASES = [
 def test_host_trace_equals_oracle(M, N, K, tile, order, G, mode, P, remap):
     s = ts.Schedule(order=order, group_m=G, mode=mode, num_programs=P, xcd_remap=remap, tile=tile)
     got = ts.schedule_trace_host(M, N, K, s)
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = (int(v) for v in tile.replace("w8", "").replace("pp", "").split("x"))
     ref = osch.trace(M, N, K, bm, bn, bk, _oracle_sched(s, P))
     assert got.shape == ref.shape
     assert np.array_equal(got, ref)
@@ -277,3 +289,11 @@ def test_mulshift_index_math_gives_the_same_map(order, G, M, N):
 def test_four_layouts_pass_validation(strides):
     # valid: rejected only because there is no device
     assert ts.gemm_raw(FAKE, FAKE, FAKE, 64, 64, 64, strides=strides) == ts.TS_ERR_NO_DEVICE
+
+def test_phase_probe_validates_before_any_hip_call():
+    sink = ctypes.c_float(0.0)
+    flops = ctypes.c_double(0.0)
+    for iters, pattern in ((0, 0), (10, -1), (10, 4)):
+        assert ts._lib.ts_mfma_phase_probe(iters, pattern, ctypes.addressof(sink), 1 << 20, ctypes.byref(flops),
+                                           None) == ts.TS_ERR_INVALID_ARG
+    assert ts._lib.ts_mfma_phase_probe(10, 2, None, 1 << 20, ctypes.byref(flops), None) == ts.TS_ERR_INVALID_ARG

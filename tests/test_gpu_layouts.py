@@ -28,10 +28,10 @@ def operands(A, B, ab, layout):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
-@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("tile", ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8", "256x256x64pp"])
 @pytest.mark.parametrize("whole", [True, False], ids=["whole", "ragged"])
 def test_layouts_integer_inputs_bit_exact(layout, tile, whole):
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = (int(v) for v in tile[:-2 if tile[-2:] in ("w8", "pp") else None].split("x"))
     M, N, K = (2 * bm, 3 * bn, 4 * bk) if whole else (2 * bm + 5, 3 * bn + 3, 3 * bk + 7)
     A, B = workloads.pair(M, N, K, "f16", "int", 800)
     C, _ = og.gemm(A, B, "f16")

@@ -7,6 +7,7 @@ the oracle's exact value rounded to the output type, bit for bit.
 """
 import ctypes
 import itertools
+import re
 
 import numpy as np
 import pytest
@@ -23,8 +24,13 @@ if torch.cuda.is_available():
 else:  # collected on CPU-only hosts, never run there
     ts = None
 
-TILES = ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8"]
+TILES = ["64x64x32", "128x128x64", "256x256x64", "256x256x64w8", "256x256x64pp"]
 IO = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+
+
+def tile_dims(tile):
+    """(BM, BN, BK) of a tile name such as "256x256x64w8"."""
+    return tuple(int(v) for v in re.match(r"(\d+)x(\d+)x(\d+)", tile).groups())
 
 
 def schedules(tile, P=256):
@@ -53,10 +59,29 @@ def assert_accept(c_gpu, C, S, c_dtype, what=""):
     return worst
 
 
+# ---- the ping-pong kernel against the 8-wave kernel ------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1536, 640), (1000, 1300, 448), (768, 512, 64)])
+@pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("bf16", "f32")])
+@pytest.mark.parametrize("mode,P", [("tiled", 0), ("persistent", 5), ("persistent", 256), ("crosstile", 3)])
+def test_pingpong_bit_identical_to_8_wave(M, N, K, ab, c_dtype, mode, P):
+    # both kernels give every accumulator its K sub-steps in the same order, so
+    # their outputs agree bit for bit, ragged tiles (edge path) included; and both
+    # are checked against the oracle's bound
+    A, B = workloads.pair(M, N, K, ab, "uniform", 520)
+    outs = []
+    for tile in ("256x256x64w8", "256x256x64pp"):
+        s = ts.Schedule(order="grouped", group_m=3, mode=mode, num_programs=P, xcd_remap=True, tile=tile)
+        outs.append(run(A, B, ab, c_dtype, s, M, N, K))
+    assert torch.equal(outs[0], outs[1])
+    C, S = og.gemm(A, B, ab, threads=4)
+    assert_accept(to_f64(outs[1]), C, S, c_dtype, "ping-pong")
+
+
 # ---- exactness with integer inputs ---------------------------------------------------
 
 SHAPES = {"64x64x32": (200, 300, 130), "128x128x64": (300, 390, 200), "256x256x64": (600, 700, 260),
-          "256x256x64w8": (600, 700, 260)}
+          "256x256x64w8": (600, 700, 260), "256x256x64pp": (600, 700, 260)}
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -77,7 +102,7 @@ def test_integer_inputs_bit_exact(tile, ab, c_dtype):
 @pytest.mark.parametrize("tile", TILES)
 def test_aligned_integer_inputs_bit_exact(tile):
     # whole tiles: the unmasked kernels
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     M, N, K = 2 * bm, 3 * bn, 4 * bk
     A, B = workloads.pair(M, N, K, "f16", "int", 501)
     C, _ = og.gemm(A, B, "f16")
@@ -107,7 +132,7 @@ def test_square_256_f16_f32_full_oracle():
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("ab,c_dtype", IO)
 def test_ragged_every_schedule(tile, ab, c_dtype):
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     M, N, K = 3 * bm + 17, 4 * bn + 9, 5 * bk + 11   # several tiles and a ragged tail in M, N, K
     A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 600)
     C, S = og.gemm(A, B, ab, threads=4)
@@ -127,7 +152,7 @@ def test_ragged_word_aligned_rows(tile, ab, c_dtype):
     # K = 6 and N = 2 (mod 8): A and B rows are 4-byte but not 16-byte aligned, and
     # so are C rows of 16-bit outputs (fp32 rows are 8-byte aligned); the masked
     # loads and stores then move 4-byte pieces
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     M, N, K = 2 * bm + 5, 3 * bn + 2, 4 * bk + 6
     A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 610)
     C, S = og.gemm(A, B, ab, threads=4)
@@ -148,7 +173,7 @@ def test_ragged_edge_paths(tile, ab, c_dtype, n_tail):
     # K a multiple of 8 with a partial last slice, M and N ragged: the direct-to-LDS
     # tiles zero-fill the edges (B rows 16-byte aligned when N = 0 mod 8, else only
     # 4-byte aligned); the 64-wide tile has no such pipeline and runs masked
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     M, N, K = 2 * bm + 5, 3 * bn + n_tail, 4 * bk + 8
     expect_path = 1 if tile == "64x64x32" else 2
     assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == expect_path
@@ -164,11 +189,11 @@ def test_ragged_edge_paths(tile, ab, c_dtype, n_tail):
             assert torch.equal(c, first), f"{sched.label()} differs from {schedules(tile)[0].label()}"
 
 
-@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8", "256x256x64pp"])
 def test_edge_path_integer_inputs_bit_exact(tile):
     # exact integer products: any wrong or missing element (a tail chunk not zeroed,
     # a row past M read, a column past N stored) shows as a mismatch
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     for (M, N, K) in ((bm + 1, bn + 2, bk + 8), (3 * bm - 7, 2 * bn + 8, 2 * bk + 56), (17, 30, 8)):
         A, B = workloads.pair(M, N, K, "f16", "int", 630)
         C, _ = og.gemm(A, B, "f16")
@@ -348,7 +373,7 @@ def test_padded_and_unaligned_operands_with_canaries(tile):
         assert (guard == -12345.0).all(), "write outside C"
 
 
-@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64", "256x256x64w8"])
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64", "256x256x64w8", "256x256x64pp"])
 @pytest.mark.parametrize("N", [296, 290], ids=["b16aligned", "b4aligned"])
 def test_edge_paths_padded_operands_with_canaries(tile, N):
     # padded row strides (8 elements) on the zero-filled-edge paths: the loads stop at
@@ -427,6 +452,13 @@ def test_mfma_loop_probe_rate():
     assert 200.0 < tf < 2600.0   # below the 2.4 GHz dense fp16 figure
 
 
+@pytest.mark.parametrize("pattern", [0, 1, 2, 3])
+def test_mfma_phase_probe_rate(pattern):
+    tf = ts.mfma_phase_tflops(pattern, iters=2000, reps=2)
+    say(f"mfma phase probe pattern {pattern}: {tf:.1f} TFLOP/s")
+    assert 200.0 < tf < 2600.0
+
+
 # ---- stream-K: split tiles, partial tiles added in a fixed order -----------------------
 
 def _streamk_run(a, b, c, sched, ws):
@@ -452,7 +484,7 @@ def _streamk_header_clean(ws, q, header):
 @pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("bf16", "f32")])
 @pytest.mark.parametrize("P", [5, 7, 64])
 def test_streamk_ragged_against_oracle(tile, ab, c_dtype, P):
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     M, N, K = 3 * bm + 17, 5 * bn + 9, 5 * bk + 11      # 4 x 6 = 24 tiles, ragged M, N, K
     A, B = workloads.pair(M, N, K, ab, "uniform" if ab == "f16" else "normal", 640)
     C, S = og.gemm(A, B, ab, threads=4)
@@ -475,7 +507,7 @@ def test_streamk_ragged_against_oracle(tile, ab, c_dtype, P):
 @pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
 def test_streamk_integer_inputs_bit_exact(tile):
     # exact products and sums: any split of K gives the exact result
-    bm, bn, bk = (int(v) for v in tile.replace("w8", "").split("x"))
+    bm, bn, bk = tile_dims(tile)
     for (M, N, K, P) in ((3 * bm + 5, 2 * bn + 8, 7 * bk + 8, 4), (2 * bm, 3 * bn, 6 * bk, 5), (17, 30, 8, 3)):
         A, B = workloads.pair(M, N, K, "f16", "int", 650)
         C, _ = og.gemm(A, B, "f16")

@@ -27,7 +27,8 @@ def _oracle(M, N, K, s, grid):
 
 
 CASES = [(256, 256, 256, "64x64x32"), (5000, 12290, 1000, "256x256x64w8"), (8192, 8192, 4096, "256x256x64w8"),
-         (16384, 16384, 128, "256x256x64w8"), (1000, 700, 0, "128x128x64"), (300, 520, 200, "64x64x32")]
+         (16384, 16384, 128, "256x256x64w8"), (1000, 700, 0, "128x128x64"), (300, 520, 200, "64x64x32"),
+         (5000, 12290, 1000, "256x256x64pp")]
 
 
 @pytest.mark.parametrize("M,N,K,tile", CASES)

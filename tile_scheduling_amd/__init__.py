@@ -33,7 +33,7 @@ TS_F16, TS_BF16, TS_F32 = 1, 2, 3
 ORDERS = {"row_major": 0, "grouped": 1, "auto": 2}
 MODES = {"tiled": 0, "persistent": 1, "crosstile": 2, "streamk": 3, "auto": 4}
 INDEX_MATH = {"divide": 0, "mulshift": 1}
-TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3, "256x256x64w8": 4}
+TILES = {"auto": 0, "64x64x32": 1, "128x128x64": 2, "256x256x64": 3, "256x256x64w8": 4, "256x256x64pp": 5}
 
 
 class _Schedule(ctypes.Structure):
@@ -68,6 +68,8 @@ _lib.ts_gemm_clocked.argtypes = _lib.ts_gemm.argtypes + [_p, _i64, _p, _i64]
 _lib.ts_gemm_clocked.restype = _i32
 _lib.ts_mfma_loop_probe.argtypes = [_i32, _p, _i64, ctypes.POINTER(ctypes.c_double), _p]
 _lib.ts_mfma_loop_probe.restype = _i32
+_lib.ts_mfma_phase_probe.argtypes = [_i32, _i32, _p, _i64, ctypes.POINTER(ctypes.c_double), _p]
+_lib.ts_mfma_phase_probe.restype = _i32
 _lib.ts_schedule_trace.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule), _p, _i64, _p]
 _lib.ts_schedule_trace.restype = _i32
 _lib.ts_schedule_trace_host.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_Schedule),
@@ -79,7 +81,7 @@ _lib.ts_status_string.argtypes = [_i32]
 _lib.ts_status_string.restype = ctypes.c_char_p
 
 EXPORTS = ("ts_gemm", "ts_gemm_workspace", "ts_gemm_noalloc", "ts_noalloc_scratch_bytes", "ts_gemm_clocked", "ts_schedule_trace", "ts_schedule_trace_host", "ts_query",
-           "ts_status_string", "ts_mfma_loop_probe")
+           "ts_status_string", "ts_mfma_loop_probe", "ts_mfma_phase_probe")
 
 
 class TsError(RuntimeError):
@@ -101,7 +103,7 @@ class Schedule:
     mode: str = "tiled"           # "tiled" | "persistent" | "crosstile" | "streamk" | "auto"
     num_programs: int = 0         # persistent grid; 0 = CUs x workgroups per CU
     xcd_remap: bool = False       # contiguous tile-id runs per XCD
-    tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64" | "256x256x64w8"
+    tile: str = "auto"            # "auto" | "64x64x32" | "128x128x64" | "256x256x64" | "256x256x64w8" | "256x256x64pp"
     index_math: str = "divide"    # "divide" | "mulshift"
 
     def _c(self) -> _Schedule:
@@ -219,22 +221,33 @@ def clock_ghz(rec) -> dict:
             "programs": int(ok.sum())}
 
 
-def mfma_loop_tflops(iters: int = 20000, reps: int = 3, device: int | str = "cuda") -> float:
-    """Sustained MFMA rate (TFLOP/s) of the no-memory probe, best of ``reps`` timed launches."""
+def _probe_tflops(launch, iters: int, reps: int, device) -> float:
     q = query(256, 256, 256)
     sink = torch.empty(q["cu_count"] * 512, dtype=torch.float32, device=device)
     flops = ctypes.c_double(0.0)
     stream = _stream_handle(sink.device)
-    _check(_lib.ts_mfma_loop_probe(iters, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream))
+    _check(launch(iters, sink, flops, stream))
     best = 0.0
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        _check(_lib.ts_mfma_loop_probe(iters, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream))
+        _check(launch(iters, sink, flops, stream))
         e1.record()
         torch.cuda.synchronize()
         best = max(best, flops.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     return best
+
+
+def mfma_loop_tflops(iters: int = 20000, reps: int = 3, device: int | str = "cuda") -> float:
+    """Sustained MFMA rate (TFLOP/s) of the no-memory probe, best of ``reps`` timed launches."""
+    return _probe_tflops(lambda n, sink, flops, stream: _lib.ts_mfma_loop_probe(
+        n, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream), iters, reps, device)
+
+
+def mfma_phase_tflops(pattern: int, iters: int = 10000, reps: int = 3, device: int | str = "cuda") -> float:
+    """MFMA rate (TFLOP/s) of the barrier-phase probe (ts_mfma_phase_probe), best of ``reps``."""
+    return _probe_tflops(lambda n, sink, flops, stream: _lib.ts_mfma_phase_probe(
+        n, pattern, sink.data_ptr(), sink.numel(), ctypes.byref(flops), stream), iters, reps, device)
 
 
 def gemm_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int,

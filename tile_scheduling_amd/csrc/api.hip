@@ -103,7 +103,8 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
     switch (cfg) {
         case CFG_64: *bm = Cfg64::BM; *bn = Cfg64::BN; *bk = Cfg64::BK; break;
         case CFG_128: *bm = Cfg128::BM; *bn = Cfg128::BN; *bk = Cfg128::BK; break;
-        case CFG_256W8: *bm = Cfg256w8::BM; *bn = Cfg256w8::BN; *bk = Cfg256w8::BK; break;
+        case CFG_256W8:
+        case CFG_256PP: *bm = Cfg256w8::BM; *bn = Cfg256w8::BN; *bk = Cfg256w8::BK; break;
         default: *bm = Cfg256::BM; *bn = Cfg256::BN; *bk = Cfg256::BK; break;
     }
 }
@@ -114,6 +115,7 @@ KernelRef kernel_of(const Plan& p) {
         case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, p.mode);
         case CFG_128: return edge ? kernels_cfg128_edge(p.io, p.path, p.mode) : kernels_cfg128(p.io, p.path, p.mode);
         case CFG_256W8: return edge ? kernels_cfg256w8_edge(p.io, p.path, p.mode) : kernels_cfg256w8(p.io, p.path, p.mode);
+        case CFG_256PP: return edge ? kernels_cfg256pp_edge(p.io, p.path, p.mode) : kernels_cfg256pp(p.io, p.path, p.mode);
         default: return edge ? kernels_cfg256_edge(p.io, p.path, p.mode) : kernels_cfg256(p.io, p.path, p.mode);
     }
 }
@@ -122,7 +124,8 @@ bool cfg_has_fast_path(int cfg) {
     switch (cfg) {
         case CFG_64: return has_fast_path<Cfg64>();
         case CFG_128: return has_fast_path<Cfg128>();
-        case CFG_256W8: return has_fast_path<Cfg256w8>();
+        case CFG_256W8:
+        case CFG_256PP: return has_fast_path<Cfg256w8>();
         default: return has_fast_path<Cfg256>();
     }
 }
@@ -241,7 +244,7 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     if (s.index_math != TS_INDEX_DIVIDE && s.index_math != TS_INDEX_MULSHIFT) return TS_ERR_INVALID_ARG;
     if (s.num_programs < 0) return TS_ERR_INVALID_ARG;
     if (s.xcd_remap != 0 && s.xcd_remap != 1) return TS_ERR_INVALID_ARG;
-    if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64_W8) return TS_ERR_INVALID_ARG;
+    if (s.tile_config < TS_TILE_AUTO || s.tile_config > TS_TILE_256x256x64_PP) return TS_ERR_INVALID_ARG;
 
     int cfg = s.tile_config;
     if (cfg == TS_TILE_AUTO) {

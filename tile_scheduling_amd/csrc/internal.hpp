@@ -12,8 +12,9 @@ namespace ts {
 // Input/output type pair of a kernel instance.
 enum : int { IO_F16_F16 = 0, IO_F16_F32 = 1, IO_BF16_BF16 = 2, IO_BF16_F32 = 3 };
 
-// Tile configurations (same numbering as TS_TILE_* in tsgemm.h).
-enum : int { CFG_64 = 1, CFG_128 = 2, CFG_256 = 3, CFG_256W8 = 4 };
+// Tile configurations (same numbering as TS_TILE_* in tsgemm.h).  CFG_256PP is the
+// 8-wave 256 x 256 x 64 tile run by the ping-pong kernel.
+enum : int { CFG_64 = 1, CFG_128 = 2, CFG_256 = 3, CFG_256W8 = 4, CFG_256PP = 5 };
 
 typedef TileCfg<64, 64, 32, 2, 2> Cfg64;
 typedef TileCfg<128, 128, 64, 2, 2> Cfg128;
@@ -97,9 +98,11 @@ KernelRef kernels_cfg64(int io, int path, int mode);
 KernelRef kernels_cfg128(int io, int path, int mode);
 KernelRef kernels_cfg256(int io, int path, int mode);
 KernelRef kernels_cfg256w8(int io, int path, int mode);
+KernelRef kernels_cfg256pp(int io, int path, int mode);
 // path PATH_EDGE (configurations with the direct-to-LDS pipeline)
 KernelRef kernels_cfg128_edge(int io, int path, int mode);
 KernelRef kernels_cfg256_edge(int io, int path, int mode);
 KernelRef kernels_cfg256w8_edge(int io, int path, int mode);
+KernelRef kernels_cfg256pp_edge(int io, int path, int mode);
 
 }  // namespace ts
