@@ -92,6 +92,17 @@ def resolved_label(q) -> str:
     return f"{o}{r}/{m}"
 
 
+def kernel_path(q, layout: str) -> int:
+    """Kernel path of the launch: ts_query plans dense [M][K] / [K][N] operands; by the
+    library's layout rules, B stored [N][K] runs whole tiles on path 3 and A stored
+    [K][M] runs the masked register path (1)."""
+    if layout[0] == "T":
+        return 1
+    if layout[1] == "T":
+        return 3 if q["masked"] == 0 else 1
+    return q["masked"]
+
+
 def sources_sha() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -217,13 +228,13 @@ def pmc_target(ts, torch, np, workloads):
 
 
 STALL_SCHEDULES = ("grouped8+remap/persistent/256x256x64w8", "grouped8+remap/persistent/256x256x64",
-                   "grouped8+remap/crosstile/256x256x64w8")
+                   "grouped8+remap/crosstile/256x256x64w8", "grouped8+remap/persistent/256x256x64pp")
 
 
 def stall_target(ts, torch, np, workloads):
     """Launch sequence for the wave-state counter passes: three launches each of the
-    8-wave and 4-wave 256x256x64 persistent kernels and the 8-wave cross-tile kernel
-    at 16384 x 16384 x 4096.  Prints a manifest line per dispatch."""
+    8-wave and 4-wave 256x256x64 persistent kernels, the 8-wave cross-tile kernel and
+    the ping-pong kernel at 16384 x 16384 x 4096.  Prints a manifest line per dispatch."""
     w = workloads.SQ_16384
     A, B = workloads.inputs(w)
     a = torch.from_numpy(A.view(np.int16)).view(torch.float16).cuda()
@@ -585,7 +596,7 @@ def main():
                    "out": w.c_dtype, "inputs": f"{w.dist} seed {w.seed}", "schedule": sched.label(),
                    "resolved_schedule": resolved_label(q),
                    "tile": f"{q['block_m']}x{q['block_n']}x{q['block_k']}", "threads": q["threads"],
-                   "grid": q["grid"], "kernel_path": q["masked"],
+                   "grid": q["grid"], "kernel_path": kernel_path(q, args.layout),
                    "executed_tflops": round(executed * args.steps / r["wall_s"] / 1e12, 2)},
         "roofline": roof,
         "clock": clock,
