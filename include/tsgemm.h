@@ -286,7 +286,9 @@ ts_status ts_gemm_clocked(const void* A, const void* B, void* C,
 /*
  * This library's own addition, a measurement probe: one workgroup of 8 waves per compute unit, each wave running
  * `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16 with no memory traffic,
- * enqueued on `stream`.  Times the matrix cores' sustained rate on this device
+ * enqueued on `stream`.  Its operands are constants held in registers, whose low
+ * toggle rate draws less power than a GEMM on random data, so its rate is an upper
+ * bound on what the matrix cores sustain, not the rate at a GEMM's power draw.  Times the matrix cores' sustained rate on this device
  * when the caller brackets it with events: *flops (host pointer) receives the
  * floating-point operations the launch executes.  `sink` is a caller-owned device
  * buffer of at least (compute units x 512) floats that receives one value per
