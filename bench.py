@@ -94,13 +94,18 @@ def resolved_label(q) -> str:
 
 def kernel_path(q, layout: str) -> int:
     """Kernel path of the launch: ts_query plans dense [M][K] / [K][N] operands; by the
-    library's layout rules, B stored [N][K] runs whole tiles on path 3 and A stored
-    [K][M] runs the masked register path (1)."""
-    if layout[0] == "T":
-        return 1
-    if layout[1] == "T":
-        return 3 if q["masked"] == 0 else 1
-    return q["masked"]
+    library's layout rules, whole tiles run path 3 with B stored [N][K], 4 with A
+    stored [K][M] and 5 with both (on tiles with the direct-to-LDS pipeline), and
+    anything else with a transposed operand the masked register path (1)."""
+    if layout == "NN":
+        return q["masked"]
+    fast = q["masked"] == 0 and q["block_k"] == 64   # whole tiles on a direct-to-LDS configuration
+    square = q["block_m"] == q["block_n"]
+    if layout == "NT":
+        return 3 if fast else 1
+    if layout == "TN":
+        return 4 if fast and square else 1
+    return 5 if fast and square else 1
 
 
 def sources_sha() -> str:

@@ -149,11 +149,12 @@ typedef struct {
     int32_t masked;                     /* kernel path: 0 whole tiles; 1 masked register        */
                                         /* pipeline (ragged or unaligned); 2 direct-to-LDS      */
                                         /* pipeline with edges zero-filled by the loads' range  */
-                                        /* checks; 3 whole tiles with B stored [N][K].          */
-                                        /* ts_query assumes dense, 16-byte aligned A [M][K] and */
-                                        /* B [K][N]; by ts_gemm's layout rules, B stored [N][K] */
-                                        /* takes path 3 where this reports 0 (else 1), and A    */
-                                        /* stored [K][M] takes path 1.                          */
+                                        /* checks; 3 whole tiles with B stored [N][K]; 4 whole  */
+                                        /* tiles with A stored [K][M]; 5 both.  ts_query        */
+                                        /* assumes dense, 16-byte aligned A [M][K] and B [K][N];*/
+                                        /* by ts_gemm's layout rules, a transposed operand      */
+                                        /* takes path 3, 4 or 5 where this reports 0 (4 and 5   */
+                                        /* on the square tiles, not 64x64x32), else path 1.     */
     int64_t workspace_bytes;            /* TS_MODE_STREAMK: workspace the launch needs (0: none) */
     int64_t trace_items;                /* most (tile, K step) items of one workgroup: the row
                                            stride of ts_schedule_trace's output                */
@@ -183,8 +184,10 @@ typedef struct {
  *   stride_cm >= N).  A dimension of extent 1 makes its stride irrelevant.  Any
  *   other stride pattern returns TS_ERR_UNSUPPORTED; a row stride below its row's
  *   length, TS_ERR_INVALID_ARG.  Whole tiles with B stored [N][K] run the
- *   direct-to-LDS pipeline with B's slices staged as A's (kernel path 3); A stored
- *   [K][M] runs the masked register pipeline, which gathers it element by element.
+ *   direct-to-LDS pipeline with B's slices staged as A's (kernel path 3); whole
+ *   tiles with A stored [K][M] run it with A's slices staged as B's (paths 4 and 5;
+ *   16-byte aligned rows).  Ragged shapes with a transposed operand run the masked
+ *   register pipeline, which gathers it element by element.
  *   ab_dtype / c_dtype: TS_F16 -> TS_F16 or TS_F32; TS_BF16 -> TS_BF16 or TS_F32.
  *   M == 0 or N == 0: nothing to do, TS_OK.  K == 0: C is set to zero.
  *   Ragged M, N, K and row strides that defeat 16-byte vector access are handled

@@ -65,27 +65,29 @@ def test_layouts_random_inputs_within_bound(layout, ab, c_dtype):
     assert ok, f"{layout}: {bad} outside the bound (worst {worst:.3g})"
 
 
-def test_nt_headline_shape_sampled():
-    # 16384 x 16384 x 4096 with B stored [N][K]: the whole-tile path that stages B as A
+@pytest.mark.parametrize("layout", ["NT", "TN", "TT"])
+def test_transposed_headline_shape_sampled(layout):
+    # 16384 x 16384 x 4096 with B stored [N][K] (the whole-tile path that stages B as A),
+    # A stored [K][M] (A staged as B) or both
     w = workloads.SQ_16384
     A, B = workloads.inputs(w)
-    a, b = operands(A, B, "f16", "NT")
+    a, b = operands(A, B, "f16", layout)
     out = {}
-    for lay, (x, y) in (("NT", (a, b)), ("NN", (to_device(A, "f16"), to_device(B, "f16")))):
+    for lay, (x, y) in ((layout, (a, b)), ("NN", (to_device(A, "f16"), to_device(B, "f16")))):
         c = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
         say(f"headline shape {lay}")
         ts.gemm(x, y, out=c, schedule=ts.Schedule(order="auto", mode="auto"))
         torch.cuda.synchronize()
         out[lay] = c
         del x, y
-    # same tiles, same K order per element: bit-identical to the [K][N] layout
-    assert torch.equal(out["NT"], out["NN"])
+    # same tiles, same K order per element: bit-identical to the [M][K] x [K][N] layout
+    assert torch.equal(out[layout], out["NN"])
     rng = np.random.default_rng(13)
     threads = max(1, min(16, og.max_threads()))
     for tm, tn in tile_sample(w.M, w.N, 256, 256, rng, n_random=16, groups=(8,)):
         r0, c0 = tm * 256, tn * 256
         C, S = og.gemm(A, B, "f16", rows=(r0, r0 + 256), cols=(c0, c0 + 256), threads=threads)
-        ok, worst, bad = og.accept(to_f64(out["NT"][r0:r0 + 256, c0:c0 + 256]), C, S, "f16")
+        ok, worst, bad = og.accept(to_f64(out[layout][r0:r0 + 256, c0:c0 + 256]), C, S, "f16")
         assert ok, f"tile ({tm}, {tn}): {bad} outside the bound"
 
 

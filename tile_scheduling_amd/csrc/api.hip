@@ -110,6 +110,13 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
 }
 
 KernelRef kernel_of(const Plan& p) {
+    if (p.path == PATH_FULL_AT || p.path == PATH_FULL_ATBT) {   // only on square direct-to-LDS tiles
+        switch (p.cfg) {
+            case CFG_128: return kernels_cfg128_at(p.io, p.path, p.mode);
+            case CFG_256: return kernels_cfg256_at(p.io, p.path, p.mode);
+            default: return kernels_cfg256w8_at(p.io, p.path, p.mode);   // the ping-pong tile runs these too
+        }
+    }
     const bool edge = p.path == PATH_EDGE;   // only on direct-to-LDS tiles
     switch (p.cfg) {
         case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, p.mode);
@@ -117,6 +124,16 @@ KernelRef kernel_of(const Plan& p) {
         case CFG_256W8: return edge ? kernels_cfg256w8_edge(p.io, p.path, p.mode) : kernels_cfg256w8(p.io, p.path, p.mode);
         case CFG_256PP: return edge ? kernels_cfg256pp_edge(p.io, p.path, p.mode) : kernels_cfg256pp(p.io, p.path, p.mode);
         default: return edge ? kernels_cfg256_edge(p.io, p.path, p.mode) : kernels_cfg256(p.io, p.path, p.mode);
+    }
+}
+
+bool cfg_has_at_path(int cfg) {
+    switch (cfg) {
+        case CFG_64: return has_at_path<Cfg64>();
+        case CFG_128: return has_at_path<Cfg128>();
+        case CFG_256W8:
+        case CFG_256PP: return has_at_path<Cfg256w8>();
+        default: return has_at_path<Cfg256>();
     }
 }
 
@@ -413,7 +430,10 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
     // Alignment levels of the rows: 16-byte operand vectors need 16-byte aligned
     // rows, 4-byte pieces 4-byte aligned ones; C vectors are 4 elements, pieces 2.
     // A stored [K][M] is gathered element by element (level 0 for its vectors).
-    p.vec_a = !a_kmaj ? 0 : (a % 16 == 0) && (lda % 8 == 0 || M == 1) ? 2
+    // A stored [K][M] is either staged whole by the direct-to-LDS loads (16-byte
+    // aligned rows) or gathered element by element (level 0 for its vectors).
+    p.vec_a = !a_kmaj ? ((a % 16 == 0) && (lda % 8 == 0) ? 2 : 0)
+              : (a % 16 == 0) && (lda % 8 == 0 || M == 1) ? 2
               : (a % 4 == 0) && (lda % 2 == 0 || M == 1) ? 1 : 0;
     p.vec_b = (b % 16 == 0) && (ldb % 8 == 0 || (b_nmaj ? K <= 1 : N <= 1)) ? 2
               : (b % 4 == 0) && (ldb % 2 == 0 || (b_nmaj ? K <= 1 : N <= 1)) ? 1 : 0;
@@ -423,13 +443,17 @@ static ts_status gemm_launch(const void* A, const void* B, void* C, int64_t M, i
                p.vec_b != 2 || p.vec_c != 2;
     // The unmasked kernels form row offsets inside a tile as 32-bit byte counts; the
     // masked ones use full-width pointers.
-    if ((int64_t)p.bm * lda * 2 > INT_MAX || (int64_t)(b_nmaj ? p.bk : p.bn) * ldb * 2 > INT_MAX) p.masked = 1;
+    if ((int64_t)(a_kmaj ? p.bm : p.bk) * lda * 2 > INT_MAX || (int64_t)(b_nmaj ? p.bk : p.bn) * ldb * 2 > INT_MAX)
+        p.masked = 1;
     if (a_kmaj && b_nmaj) {
         p.path = choose_path(p, N, K, a, b, lda, ldb);
     } else if (a_kmaj && !p.masked && cfg_has_fast_path(p.cfg)) {
         p.path = PATH_FULL_BT;   // whole tiles, B stored [N][K] (its rows 16-byte aligned)
+    } else if (!a_kmaj && !p.masked && cfg_has_at_path(p.cfg)) {
+        // whole tiles, A stored [K][M] (its rows 16-byte aligned), B either way
+        p.path = b_nmaj ? PATH_FULL_AT : PATH_FULL_ATBT;
     } else {
-        p.path = PATH_MASKED;    // A stored [K][M], or ragged / unaligned with B stored [N][K]
+        p.path = PATH_MASKED;    // ragged or unaligned with a transposed operand; the 64x64x32 tile
         p.masked = true;
     }
 

@@ -67,8 +67,9 @@ struct GemmArgs {
     const uint16_t* B;
     void* C;
     int M, N, K;
-    long long lda, ldb, ldc;  // strides between the stored rows, in elements: A [M][K] (lda = stride_am),
-                              // B [K][N] (ldb = stride_bk) or, on PATH_FULL_BT, B stored [N][K] (ldb =
+    long long lda, ldb, ldc;  // strides between the stored rows, in elements: A [M][K] (lda = stride_am)
+                              // or, on PATH_FULL_AT(BT), A stored [K][M] (lda = stride_ak); B [K][N]
+                              // (ldb = stride_bk) or, on PATH_FULL_(AT)BT, B stored [N][K] (ldb =
                               // stride_bn); C [M][N]
     long long sam, sak, sbk, sbn;  // all four element strides (the masked path gathers with them)
     // Row alignment of A, B (16-bit elements) and C: 2 if rows allow 16-byte (A, B) /
@@ -293,14 +294,16 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* lds, uint32_t off) {
 // Kernel paths: whole tiles; masked register pipeline (any operand layout); direct-
 // to-LDS pipeline with ragged edges zero-filled by the loads' range checks; whole
 // tiles with B stored [N][K] (K contiguous, as A), whose B slices are staged and read
-// exactly as A's.
-enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE = 2, PATH_FULL_BT = 3 };
+// exactly as A's; whole tiles with A stored [K][M] (M contiguous, as B), whose A
+// slices are staged and read exactly as B's (with B stored [K][N] or [N][K]).
+enum : int { PATH_FULL = 0, PATH_MASKED = 1, PATH_EDGE = 2, PATH_FULL_BT = 3, PATH_FULL_AT = 4, PATH_FULL_ATBT = 5 };
 
 template <class Cfg, class TI, class TO, int PATH>
 struct Engine {
     static constexpr bool MASKED = PATH == PATH_MASKED;
     static constexpr bool EDGE = PATH == PATH_EDGE;
-    static constexpr bool BT = PATH == PATH_FULL_BT;   // B stored [N][K]
+    static constexpr bool BT = PATH == PATH_FULL_BT || PATH == PATH_FULL_ATBT;   // B stored [N][K]
+    static constexpr bool AT = PATH == PATH_FULL_AT || PATH == PATH_FULL_ATBT;   // A stored [K][M]
     static constexpr bool EDGES = PATH != PATH_FULL;   // C stores masked to M x N
     static constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     static constexpr int FM = Cfg::FM, FN = Cfg::FN, KCH = Cfg::KCH, SUB = Cfg::SUB;
@@ -323,10 +326,13 @@ struct Engine {
     static constexpr int B_DMA_N = !FAST ? 0 : BT ? BN * RB / 1024 / NW   // 1 KiB B loads per wave
                                                   : BK * RBB / 1024 / NW;
     static_assert(!BT || FAST, "B stored [N][K] runs on the direct-to-LDS pipeline");
+    // A stored [K][M]: its [k][m] slices have the geometry of B's [k][n] slices
+    static_assert(!AT || (FAST && BM == BN), "A stored [K][M] runs on the direct-to-LDS pipeline of square tiles");
     static constexpr int DA = FAST ? 2 : 1;          // A slices in flight ahead of the multiplied one
     static constexpr int DB = FAST ? 2 : 1;          // B slices in flight ahead of the multiplied one
     static constexpr int NFB = FAST ? 4 : 2;         // fragment register buffers
     static constexpr int NJB = FN < 4 ? FN : 4;      // per-lane B transpose-read offsets
+    static constexpr int NIA = FM < 4 ? FM : 4;      // per-lane A transpose-read offsets (A stored [K][M])
     // sub-steps that write the next slice into LDS (register path)
     static constexpr int A_STORE_S = SUB > 2 ? SUB - 2 : SUB - 1;
     static constexpr int B_STORE_S = SUB - 1;
@@ -343,6 +349,8 @@ struct Engine {
     uint32_t b_rd[SUB];   // register path: B fragment read, as a_rd
     uint32_t bt_rd[NJB];  // fast path: B transpose read of block u (block j: bt_rd[j % 4] + (j / 4) * 256)
     uint32_t b_dg[2];     // fast path: B load global offset, by bit 3 of its first row
+    uint32_t at_rd[NIA];  // A stored [K][M]: A transpose read of block u, as bt_rd
+    uint32_t a_dg[2];     // A stored [K][M]: A load global offset, as b_dg
     uint32_t a_wr[2];     // register path: A chunk c at a_wr[c&1] + c*A_ROWS_PER_C*RB
     uint32_t b_wr[8];     // B write j of the loader block (see b_wr_at)
     uint32_t b_sel[2];    // register path: byte-permute selector of B writes with even / odd j
@@ -424,6 +432,15 @@ struct Engine {
                 const int r = 8 * e2 + wave * RPD + rl;
                 const int fr = (4 * (r & 3)) ^ (2 * ((r >> 3) & 1));
                 b_dg[e2] = (uint32_t)(((long long)rl * g.ldb + (pch ^ fr) * 8) * 2);
+                a_dg[e2] = (uint32_t)(((long long)rl * g.lda + (pch ^ fr) * 8) * 2);
+            }
+            // A stored [K][M]: its [k][m] slot is filled and read exactly as B's [k][n]
+            // slot, with 32-row blocks of m in place of 32-column blocks of n
+#pragma unroll
+            for (int u = 0; u < NIA; ++u) {
+                const int W = wm * FM + u;   // 32-row block within the tile
+                const int chunk = ((4 * W) | (2 * qn + (a >> 1))) ^ ff;
+                at_rd[u] = (uint32_t)((8 * qh + e) * RBB + chunk * 16 + (a & 1) * 8);
             }
             b_wr[0] = 0;
             b_sel[0] = b_sel[1] = 0;
@@ -471,8 +488,12 @@ struct Engine {
         // register.
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-            asm volatile("" : "+v"(a_rd[s]));
+            if (!AT) asm volatile("" : "+v"(a_rd[s]));
             if (!FAST || BT) asm volatile("" : "+v"(b_rd[s]));
+        }
+        if (AT) {
+#pragma unroll
+            for (int u = 0; u < NIA; ++u) asm volatile("" : "+v"(at_rd[u]));
         }
         if (FAST && !BT) {
 #pragma unroll
@@ -554,6 +575,12 @@ struct Engine {
     // paths: chunks at or past k = klim of the slice read as zero.
     template <int SLOT>
     __device__ __forceinline__ void dma_a_one(int c, const __amdgpu_buffer_rsrc_t& r) {
+        if constexpr (AT) {   // as B's [k][n] loads, over A's [k][m] rows
+            const int grp = c * NW + wave;
+            const int e = ((c * NW * RPD) >> 3) & 1;
+            dma16(r, a_dg[e], (int)((long long)grp * RPD * g.lda * 2), la[SLOT] + grp * 1024);
+            return;
+        }
         const int grp = c * NW + wave;                     // 8-row group (1 KiB)
         const int e = ((c * NW) >> 2) & 1;
         if constexpr (EDGE) {
@@ -563,9 +590,13 @@ struct Engine {
             dma16(r, a_go[e], (int)((long long)grp * 8 * g.lda * 2), la[SLOT] + grp * 1024);
         }
     }
+    // Element offset of A's slice k of tile row m0 (the slice's first element).
+    __device__ __forceinline__ long long a_slice(int m0, int k) const {
+        return AT ? (long long)k * BK * g.lda + m0 : (long long)m0 * g.lda + k * BK;
+    }
     template <int SLOT>
     __device__ __forceinline__ void dma_a(int m0, int k, int valid) {
-        const __amdgpu_buffer_rsrc_t r = rsrc_a((long long)m0 * g.lda + k * BK, valid);
+        const __amdgpu_buffer_rsrc_t r = rsrc_a(a_slice(m0, k), valid);
         if constexpr (EDGE) klim = g.K - k * BK;
 #pragma unroll
         for (int c = 0; c < A_DMA_N; ++c) dma_a_one<SLOT>(c, r);
@@ -711,6 +742,12 @@ struct Engine {
     // A fragment of 32-row block i at sub-step s from slot SLOT.
     template <int SLOT>
     __device__ __forceinline__ u32x4 read_a(int s, int i) const {
+        if constexpr (AT) {   // two transpose reads, as read_b's
+            const char* tb = la[SLOT] + (i >> 2) * 256 + 16 * s * RBB;
+            const u32x2 lo = lds_read_tr(tb, at_rd[i & 3]);
+            const u32x2 hi = lds_read_tr(tb + 4 * RBB, at_rd[i & 3]);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
         const char* base = la[SLOT];
         return lds_read16(base, a_rd[(KCH == 8 && (i & 1)) ? (s ^ 2) : s] + i * 32 * RB);
     }
@@ -915,7 +952,7 @@ struct Engine {
     __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false) {
         if constexpr (FAST) {
             const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_slice(nx.n0, nx.kb), nx.vb);
-            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a((long long)nx.m0 * g.lda + nx.ka * BK, nx.va);
+            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_slice(nx.m0, nx.ka), nx.va);
             if constexpr (EDGE) klim = g.K - nx.ka * BK;
             fast_sub<SLOT, 0>(ra_, rb_);
             fast_sub<SLOT, 1>(ra_, rb_);

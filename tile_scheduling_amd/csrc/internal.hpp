@@ -68,22 +68,41 @@ const void* kernel_by_path_edge(int path, int mode) {
     return kernel_by_mode<Cfg, TI, TO, PATH_EDGE>(mode);
 }
 
-template <class Cfg, class TI, class TO, bool EDGE>
+// Whole-tile instances with A stored [K][M] (B stored [K][N] or [N][K]): square
+// direct-to-LDS tiles only.
+template <class Cfg, class TI, class TO>
+const void* kernel_by_path_at(int path, int mode) {
+    if constexpr (Engine<Cfg, TI, TO, PATH_FULL>::FAST_OK && Cfg::BM == Cfg::BN) {
+        if (path == PATH_FULL_ATBT) return kernel_by_mode<Cfg, TI, TO, PATH_FULL_ATBT>(mode);
+        return kernel_by_mode<Cfg, TI, TO, PATH_FULL_AT>(mode);
+    } else {
+        (void)path;
+        (void)mode;
+        return nullptr;
+    }
+}
+
+// Instance groups, one per translation unit of a tile configuration.
+enum : int { KG_BASE = 0, KG_EDGE = 1, KG_AT = 2 };
+
+template <class Cfg, class TI, class TO, int KG>
 const void* kernel_by_path(int path, int mode) {
-    if constexpr (EDGE)
+    if constexpr (KG == KG_EDGE)
         return kernel_by_path_edge<Cfg, TI, TO>(path, mode);
+    else if constexpr (KG == KG_AT)
+        return kernel_by_path_at<Cfg, TI, TO>(path, mode);
     else
         return kernel_by_path_base<Cfg, TI, TO>(path, mode);
 }
 
-template <class Cfg, bool EDGE>
+template <class Cfg, int KG>
 KernelRef kernel_for(int io, int path, int mode) {
     const void* f = nullptr;
     switch (io) {
-        case IO_F16_F16: f = kernel_by_path<Cfg, InF16, OutF16, EDGE>(path, mode); break;
-        case IO_F16_F32: f = kernel_by_path<Cfg, InF16, OutF32, EDGE>(path, mode); break;
-        case IO_BF16_BF16: f = kernel_by_path<Cfg, InBF16, OutBF16, EDGE>(path, mode); break;
-        default: f = kernel_by_path<Cfg, InBF16, OutF32, EDGE>(path, mode); break;
+        case IO_F16_F16: f = kernel_by_path<Cfg, InF16, OutF16, KG>(path, mode); break;
+        case IO_F16_F32: f = kernel_by_path<Cfg, InF16, OutF32, KG>(path, mode); break;
+        case IO_BF16_BF16: f = kernel_by_path<Cfg, InBF16, OutBF16, KG>(path, mode); break;
+        default: f = kernel_by_path<Cfg, InBF16, OutF32, KG>(path, mode); break;
     }
     return KernelRef{f, Cfg::NT, Cfg::LDS_BYTES};
 }
@@ -91,6 +110,9 @@ KernelRef kernel_for(int io, int path, int mode) {
 // Whether a configuration has the direct-to-LDS pipeline (and so the edge paths).
 template <class Cfg>
 constexpr bool has_fast_path() { return Engine<Cfg, InF16, OutF16, PATH_FULL>::FAST_OK; }
+// Whether it has the whole-tile paths with A stored [K][M].
+template <class Cfg>
+constexpr bool has_at_path() { return has_fast_path<Cfg>() && Cfg::BM == Cfg::BN; }
 
 // One function per tile configuration, each defined in its own translation unit.
 // path PATH_FULL, PATH_FULL_BT or PATH_MASKED
@@ -99,6 +121,10 @@ KernelRef kernels_cfg128(int io, int path, int mode);
 KernelRef kernels_cfg256(int io, int path, int mode);
 KernelRef kernels_cfg256w8(int io, int path, int mode);
 KernelRef kernels_cfg256pp(int io, int path, int mode);
+// path PATH_FULL_AT or PATH_FULL_ATBT (square direct-to-LDS configurations)
+KernelRef kernels_cfg128_at(int io, int path, int mode);
+KernelRef kernels_cfg256_at(int io, int path, int mode);
+KernelRef kernels_cfg256w8_at(int io, int path, int mode);
 // path PATH_EDGE (configurations with the direct-to-LDS pipeline)
 KernelRef kernels_cfg128_edge(int io, int path, int mode);
 KernelRef kernels_cfg256_edge(int io, int path, int mode);

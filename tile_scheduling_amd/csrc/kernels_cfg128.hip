@@ -3,5 +3,5 @@
 #include "internal.hpp"
 
 namespace ts {
-KernelRef kernels_cfg128(int io, int path, int mode) { return kernel_for<Cfg128, false>(io, path, mode); }
+KernelRef kernels_cfg128(int io, int path, int mode) { return kernel_for<Cfg128, KG_BASE>(io, path, mode); }
 }  // namespace ts

@@ -3,5 +3,5 @@
 #include "internal.hpp"
 
 namespace ts {
-KernelRef kernels_cfg256w8(int io, int path, int mode) { return kernel_for<Cfg256w8, false>(io, path, mode); }
+KernelRef kernels_cfg256w8(int io, int path, int mode) { return kernel_for<Cfg256w8, KG_BASE>(io, path, mode); }
 }  // namespace ts

@@ -3,5 +3,5 @@
 #include "internal.hpp"
 
 namespace ts {
-KernelRef kernels_cfg256w8_edge(int io, int path, int mode) { return kernel_for<Cfg256w8, true>(io, path, mode); }
+KernelRef kernels_cfg256w8_edge(int io, int path, int mode) { return kernel_for<Cfg256w8, KG_EDGE>(io, path, mode); }
 }  // namespace ts

@@ -25,7 +25,7 @@ struct Slice {
 template <class E>
 __device__ __forceinline__ Slice<E> slice_rsrc(E& e, int m0, int n0, int k, int valid = -1) {
     if constexpr (E::EDGE) e.klim = e.g.K - k * E::BK;
-    return Slice<E>{e.rsrc_a((long long)m0 * e.g.lda + k * E::BK, valid), e.rsrc_b(e.b_slice(n0, k), valid)};
+    return Slice<E>{e.rsrc_a(e.a_slice(m0, k), valid), e.rsrc_b(e.b_slice(n0, k), valid)};
 }
 
 // This wave's load number c (B loads first, then A) of a slice into slot SLOT.
