@@ -50,6 +50,25 @@ def test_layouts_integer_inputs_bit_exact(layout, tile, whole):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+def test_layouts_nested_crosstile_bit_exact(layout, tile):
+    # 8 K steps per tile: the cross-tile mode runs the nested kernel on every layout
+    bm, bn, bk = (int(v) for v in tile[:-2 if tile[-2:] in ("w8", "pp") else None].split("x"))
+    M, N, K = 2 * bm, 3 * bn, 8 * bk
+    A, B = workloads.pair(M, N, K, "f16", "int", 820)
+    C, _ = og.gemm(A, B, "f16")
+    a, b = operands(A, B, "f16", layout)
+    for P in (1, 4):
+        s = ts.Schedule(order="grouped", group_m=2, mode="crosstile", num_programs=P, tile=tile)
+        say(f"layout {layout} {M}x{N}x{K} {s.label()}")
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ts.gemm(a, b, out=c, schedule=s)
+        torch.cuda.synchronize()
+        bad = np.argwhere(to_f64(c) != C)
+        assert bad.size == 0, f"{layout} P={P}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("bf16", "f32"), ("bf16", "bf16")])
 def test_layouts_random_inputs_within_bound(layout, ab, c_dtype):
     M, N, K = 700, 900, 333

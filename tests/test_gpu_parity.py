@@ -202,6 +202,57 @@ def test_edge_path_integer_inputs_bit_exact(tile):
             assert np.array_equal(got, C), (M, N, K, mode)
 
 
+# ---- the nested cross-tile kernel (an even number of at least 8 K steps) -----------
+
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+@pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("shape", ["whole", "edges"])
+def test_nested_crosstile_integer_inputs_bit_exact(tile, ab, c_dtype, shape):
+    # cross-tile mode with 8 or 10 K steps per tile runs the nested kernel, whose last
+    # K step of a tile does not wait for the next slice and whose post-epilogue wait
+    # counts the stores of the tile just stored (edge tiles: none counted); one, a
+    # few and many tiles per program; exact integer products, and bit-identical to
+    # the persistent kernel
+    bm, bn, bk = tile_dims(tile)
+    M, N, K = (3 * bm, 5 * bn, 8 * bk) if shape == "whole" else (3 * bm + 5, 4 * bn + 8, 9 * bk + 8)
+    A, B = workloads.pair(M, N, K, ab, "int", 640)
+    C, _ = og.gemm(A, B, ab, threads=4)
+    expect = round_to(C, c_dtype)
+    assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == (0 if shape == "whole" else 2)
+    for P in (1, 4, 15):
+        outs = []
+        for mode in ("crosstile", "persistent"):
+            s = ts.Schedule(order="grouped", group_m=2, mode=mode, num_programs=P, xcd_remap=True, tile=tile)
+            got = run(A, B, ab, c_dtype, s, M, N, K)
+            bad = np.argwhere(to_f64(got) != expect)
+            assert bad.size == 0, f"{s.label()}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+            outs.append(got)
+        assert torch.equal(outs[0], outs[1])
+
+
+def test_nested_crosstile_random_inputs_back_to_back():
+    # random fp16 inputs, ragged, 16 K steps per tile: two different products launched
+    # back to back on one stream, each against the oracle's bound, and the auto
+    # schedule (cross-tile) bit-identical to persistent
+    outs = []
+    for seed, (M, N, K) in ((650, (1300, 2048, 1024)), (651, (2000, 1100, 1000))):
+        A, B = workloads.pair(M, N, K, "f16", "uniform", seed)
+        C, S = og.gemm(A, B, "f16", threads=4)
+        a, b = to_device(A, "f16"), to_device(B, "f16")
+        q = ts.query(M, N, K, ts.Schedule(order="auto", mode="auto", tile="256x256x64w8"))
+        assert q["mode"] == 2, q
+        c = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ts.gemm(a, b, out=c, schedule=ts.Schedule(order="auto", mode="auto", tile="256x256x64w8"))
+        outs.append((c, C, S, a, b, M, N))
+    torch.cuda.synchronize()
+    for c, C, S, a, b, M, N in outs:
+        assert_accept(to_f64(c), C, S, "f16", f"{M}x{N}")
+        p = torch.empty_like(c)
+        ts.gemm(a, b, out=p, schedule=ts.Schedule(order="auto", mode="persistent", tile="256x256x64w8"))
+        torch.cuda.synchronize()
+        assert torch.equal(c, p)
+
+
 # ---- the ragged bf16 workload at full size: all four schedules -----------------------
 
 def test_ragged_bf16_5000x12290x1000_full_size():

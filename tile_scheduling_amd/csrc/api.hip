@@ -109,21 +109,40 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
     }
 }
 
+// The nested cross-tile kernel (MODE_XTILE) runs the cross-tile mode on the 128 x
+// 128 and 8-wave 256 x 256 direct-to-LDS tiles when a tile has an even number of
+// at least this many K steps; with fewer, its epilogues come so close together
+// that the deeper queue of stores slows the loads behind them (measured on the
+// 16384^2 product: 10 % slower than the flattened loop at 2 steps, 2-3 % at 4 and
+// 6, 4 % faster at 8).
+constexpr int kXtileMinSteps = 8;
+bool xtile_shape(int cfg, int64_t ks) {
+    return (cfg == CFG_128 || cfg == CFG_256W8) && ks >= kXtileMinSteps && ks % 2 == 0;
+}
+
+// Kernel mode of a plan: MODE_XTILE where the nested cross-tile kernel runs, else
+// the plan's own mode.
+int kernel_mode(const Plan& p) {
+    if (p.mode == TS_MODE_CROSSTILE && p.path != PATH_MASKED && xtile_shape(p.cfg, p.s.ks)) return MODE_XTILE;
+    return p.mode;
+}
+
 KernelRef kernel_of(const Plan& p) {
+    const int km = kernel_mode(p);
     if (p.path == PATH_FULL_AT || p.path == PATH_FULL_ATBT) {   // only on square direct-to-LDS tiles
         switch (p.cfg) {
-            case CFG_128: return kernels_cfg128_at(p.io, p.path, p.mode);
-            case CFG_256: return kernels_cfg256_at(p.io, p.path, p.mode);
-            default: return kernels_cfg256w8_at(p.io, p.path, p.mode);   // the ping-pong tile runs these too
+            case CFG_128: return kernels_cfg128_at(p.io, p.path, km);
+            case CFG_256: return kernels_cfg256_at(p.io, p.path, km);
+            default: return kernels_cfg256w8_at(p.io, p.path, km);   // the ping-pong tile runs these too
         }
     }
     const bool edge = p.path == PATH_EDGE;   // only on direct-to-LDS tiles
     switch (p.cfg) {
-        case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, p.mode);
-        case CFG_128: return edge ? kernels_cfg128_edge(p.io, p.path, p.mode) : kernels_cfg128(p.io, p.path, p.mode);
-        case CFG_256W8: return edge ? kernels_cfg256w8_edge(p.io, p.path, p.mode) : kernels_cfg256w8(p.io, p.path, p.mode);
-        case CFG_256PP: return edge ? kernels_cfg256pp_edge(p.io, p.path, p.mode) : kernels_cfg256pp(p.io, p.path, p.mode);
-        default: return edge ? kernels_cfg256_edge(p.io, p.path, p.mode) : kernels_cfg256(p.io, p.path, p.mode);
+        case CFG_64: return kernels_cfg64(p.io, edge ? PATH_MASKED : p.path, km);
+        case CFG_128: return edge ? kernels_cfg128_edge(p.io, p.path, km) : kernels_cfg128(p.io, p.path, km);
+        case CFG_256W8: return edge ? kernels_cfg256w8_edge(p.io, p.path, km) : kernels_cfg256w8(p.io, p.path, km);
+        case CFG_256PP: return edge ? kernels_cfg256pp_edge(p.io, p.path, km) : kernels_cfg256pp(p.io, p.path, km);
+        default: return edge ? kernels_cfg256_edge(p.io, p.path, km) : kernels_cfg256(p.io, p.path, km);
     }
 }
 
@@ -277,8 +296,11 @@ ts_status plan_shape(int64_t M, int64_t N, int64_t K, int32_t ab, int32_t c, con
     cfg_dims(cfg, &p->bm, &p->bn, &p->bk);
     const int64_t nm = cdiv64(M, p->bm), nn = cdiv64(N, p->bn), ks = cdiv64(K, p->bk);
     if (nm * nn > INT_MAX / 2 || ks > INT_MAX / 2) return TS_ERR_UNSUPPORTED;
-    if (s.mode == TS_MODE_AUTO)   // the merged loop pays where tiles are short (small K)
-        s.mode = (ks <= kCrossTileMaxSteps && cfg != CFG_256) ? TS_MODE_CROSSTILE : TS_MODE_PERSISTENT;
+    // the merged loop pays where tiles are short (small K), and at any K where the
+    // nested cross-tile kernel runs (its epilogue overlaps the next tile's loads)
+    if (s.mode == TS_MODE_AUTO)
+        s.mode = ((ks <= kCrossTileMaxSteps && cfg != CFG_256) || xtile_shape(cfg, ks)) ? TS_MODE_CROSSTILE
+                                                                                          : TS_MODE_PERSISTENT;
     p->mode = s.mode;
     p->requested_programs = s.num_programs;
     p->s.nm = (int)nm;

@@ -948,16 +948,24 @@ struct Engine {
     // `after_store`: the epilogue stores of the tile before were issued after the
     // loads this barrier waits for; they may stay in flight.  Not on the edge paths:
     // their masked epilogue issues a varying number of stores, so they wait for all.
-    template <int SLOT>
-    __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false) {
+    // ENDS (fast path): the last K step of a tile whose epilogue follows, in a loop
+    // that reads the next slice's first fragments again after the epilogue; its
+    // barrier then only has to certify that every wave has finished reading this
+    // slot, and the wait for the next slice moves behind the epilogue.
+    // `sc`: store class of the tile before (store_class), default the unmasked
+    // count (edge path: none counted).
+    template <int SLOT, bool ENDS = false>
+    __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false, int sc = EDGE ? 0 : 1) {
         if constexpr (FAST) {
             const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_slice(nx.n0, nx.kb), nx.vb);
             const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_slice(nx.m0, nx.ka), nx.va);
             if constexpr (EDGE) klim = g.K - nx.ka * BK;
             fast_sub<SLOT, 0>(ra_, rb_);
             fast_sub<SLOT, 1>(ra_, rb_);
-            if (!EDGE && after_store)
-                barrier_after_loads<(NST < 63 ? NST : 63)>();
+            if constexpr (ENDS)
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else if (after_store)
+                barrier_behind_stores<0>(sc);
             else
                 barrier_after_loads<0>();
             fast_sub<SLOT, 2>(ra_, rb_);
@@ -978,6 +986,40 @@ struct Engine {
     __device__ __forceinline__ void reread_frags() {
         read_frags<SLOT>(0, 0);
         read_frags<SLOT>(1, 1);
+    }
+
+    // Fast path: the loads of slices p0 (slot 0) and p1 (slot 1), nothing waited for.
+    __device__ __forceinline__ void prologue_loads(const Next& p0, const Next& p1) {
+        dma_b<0>(p0.n0, p0.kb, -1);
+        dma_a<0>(p0.m0, p0.ka, -1);
+        dma_b<1>(p1.n0, p1.kb, p1.vb);
+        dma_a<1>(p1.m0, p1.ka, p1.va);
+    }
+    // Loads of one slice, per wave.
+    static constexpr int NLD = A_DMA_N + B_DMA_N;
+
+    // Store class of the tile at (m0, n0): 1 if each wave's epilogue issues at least
+    // NST store instructions, else 0 (nothing counted).  The unmasked epilogue
+    // issues exactly NST.  The masked one issues at least one store per 16-byte
+    // chunk on a tile inside M x N (the pieces of a chunk that C's alignment calls
+    // for are merged back into one store by the compiler, so no more are counted),
+    // and a varying number on an edge tile.
+    __device__ __forceinline__ int store_class(int m0, int n0) const {
+        if constexpr (!EDGES)
+            return 1;
+        else
+            return (m0 + BM <= g.M && n0 + BN <= g.N) ? 1 : 0;
+    }
+    // Barrier after a wait that lets the last EXTRA + sc * NST VMEM operations of
+    // this wave stay in flight: EXTRA loads issued after the ones waited for, then
+    // the epilogue stores of a tile of store class sc.
+    template <int EXTRA>
+    __device__ __forceinline__ void barrier_behind_stores(int sc) {
+        constexpr int W = EXTRA + NST < 63 ? EXTRA + NST : 63;
+        if (sc)
+            barrier_after_loads<W>();
+        else
+            barrier_after_loads<EXTRA>();
     }
 
     // Prologue: slice p0 in slot 0 with the fragments of its first sub-step read
@@ -1424,6 +1466,84 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
         while (it < total) {
             step(S0{});
             step(S1{});
+        }
+    }
+    e.drain();
+    pc.stop(g);
+}
+
+// Cross-tile mode on the direct-to-LDS tiles with an even number (at least two) of
+// K steps per tile: the same (tile, k) sequence as the flattened loop, run as a
+// loop over the program's tiles with the K loop inside, so that the per-step work
+// has no cursor to advance.  The loads stay two items ahead, so the last two K
+// steps of a tile load the first two slices of the next one, and those are in
+// flight while the tile is stored.  The last K step of a tile does not wait for
+// the next slice at its barrier (the fragments it reads ahead are read again);
+// that wait comes after the epilogue, where this tile's stores, issued after the
+// loads it waits for, may stay in flight: a wave then waits only for the stores
+// of the tile before, one tile earlier, instead of those it has just issued
+// (loads and stores retire in issue order on one counter).
+template <class Cfg, class TI, class TO, int PATH>
+__global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
+    __shared__ __attribute__((aligned(16))) char lds_c[Cfg::C_BYTES > 0 ? Cfg::C_BYTES : 16];
+    typedef Engine<Cfg, TI, TO, PATH> E;
+    static_assert(E::FAST && E::DA == 2 && E::DB == 2, "direct-to-LDS pipeline, two slices ahead");
+    E e(g, lds_a0, lds_a1, lds_b0, lds_b1, lds_c);
+    ProgramClock pc;
+    pc.start(g);
+    const ProgramWork w(g.s, blockIdx.x);
+    const int nt = w.ntiles, ks = w.ksp;
+    if (nt == 0) {
+        pc.stop(g);
+        return;
+    }
+    int m0, n0, m1 = 0, n1 = 0;   // this tile and the next
+    int sc = 0;                   // store class of the tile before
+    {
+        int tm, tn;
+        tile_coords(g.s, w.tile_id(0), tm, tn);
+        m0 = tm * Cfg::BM;
+        n0 = tn * Cfg::BN;
+        if (nt > 1) {
+            tile_coords(g.s, w.tile_id(1), tm, tn);
+            m1 = tm * Cfg::BM;
+            n1 = tn * Cfg::BN;
+        }
+    }
+    e.prologue_loads(typename E::Next{m0, 0, -1, n0, 0, -1}, typename E::Next{m0, 1, -1, n0, 1, -1});
+    for (int i = 0; i < nt; ++i) {
+        const int vn = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
+        // loads of K step k: item (i, k + 2), in the next tile from k = ks - 2 on;
+        // integer masks keep the choice in scalar registers
+        auto nx = [&](int k) {
+            const int nxt = ~E::vmask(k + 2, ks);   // -1: the item is in the next tile
+            const int mm = m0 + ((m1 - m0) & nxt), nn = n0 + ((n1 - n0) & nxt);
+            const int kk = k + 2 - (ks & nxt);
+            const int vm = (vn & nxt) | ~nxt;
+            return typename E::Next{mm, kk, vm, nn, kk, vm};
+        };
+        // the first slice of this tile has landed; behind it are its second slice
+        // and the stores of the tile before, which may stay in flight
+        e.template barrier_behind_stores<E::NLD>(sc);
+        e.template reread_frags<0>();
+        e.zero_acc();
+        e.template kstep<0>(nx(0), i > 0, sc);
+        for (int k = 1; k < ks - 1; k += 2) {
+            e.template kstep<1>(nx(k));
+            e.template kstep<0>(nx(k + 1));
+        }
+        e.template kstep<1, true>(nx(ks - 1));
+        e.store_tile(m0, n0);
+        sc = e.store_class(m0, n0);
+        m0 = m1;
+        n0 = n1;
+        if (i + 2 < nt) {
+            int tm, tn;
+            tile_coords(g.s, w.tile_id(i + 2), tm, tn);
+            m1 = tm * Cfg::BM;
+            n1 = tn * Cfg::BN;
         }
     }
     e.drain();

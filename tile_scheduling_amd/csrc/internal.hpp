@@ -39,6 +39,11 @@ const void* kernel_by_mode(int mode) {
         case MODE_TILED: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_TILED>);
         case MODE_PERSISTENT: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_PERSISTENT>);
         case MODE_STREAMK: return reinterpret_cast<const void*>(&gemm_tiles_kernel<Cfg, TI, TO, PATH, MODE_STREAMK>);
+        case MODE_XTILE:
+            if constexpr (has_flat_kernel<Cfg>() && Engine<Cfg, TI, TO, PATH>::FAST)
+                return reinterpret_cast<const void*>(&gemm_xtile_kernel<Cfg, TI, TO, PATH>);
+            else
+                return nullptr;
         default:
             if constexpr (has_flat_kernel<Cfg>())
                 return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);
