@@ -95,7 +95,7 @@ enum {
        summation order along K).  Needs a workspace: ts_gemm_workspace, sized by
        ts_query's workspace_bytes (0 when no tile is split). */
     TS_MODE_STREAMK = 3,
-    /* chosen by the library: TS_MODE_CROSSTILE when a tile has at most 16 K
+    /* chosen by the library: TS_MODE_CROSSTILE when a tile has at most 32 K
        steps (the cross-tile page finds the merged loop paying where the tile
        boundary is a large share of the work, i.e. at small K), else
        TS_MODE_PERSISTENT.  ts_query reports the resolved mode. */

@@ -262,8 +262,9 @@ def test_auto_order_is_the_models_choice(M, N, K, tile, mode, P):
         assert np.array_equal(ts.schedule_trace_host(M, N, K, auto), ts.schedule_trace_host(M, N, K, sched))
 
 
-@pytest.mark.parametrize("K,expect", [(128, "crosstile"), (1024, "crosstile"), (1025, "persistent"),
-                                      (4096, "persistent"), (0, "crosstile")])
+@pytest.mark.parametrize("K,expect", [(128, "crosstile"), (1024, "crosstile"), (1025, "crosstile"),
+                                      (2048, "crosstile"), (2049, "persistent"), (4096, "persistent"),
+                                      (0, "crosstile")])
 def test_auto_mode_by_k_steps(K, expect):
     q = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256, tile="256x256x64w8"))
     assert q["mode"] == {"persistent": 1, "crosstile": 2}[expect]
