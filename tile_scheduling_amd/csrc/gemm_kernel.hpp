@@ -957,9 +957,26 @@ struct Engine {
     template <int SLOT, bool ENDS = false>
     __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false, int sc = EDGE ? 0 : 1) {
         if constexpr (FAST) {
-            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_slice(nx.n0, nx.kb), nx.vb);
-            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_slice(nx.m0, nx.ka), nx.va);
-            if constexpr (EDGE) klim = g.K - nx.ka * BK;
+            kstep_at<SLOT, ENDS>(a_slice(nx.m0, nx.ka), b_slice(nx.n0, nx.kb), nx.ka, nx.va, after_store, sc);
+            return;
+        }
+        constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
+        substeps<SLOT>(nx, std::make_integer_sequence<int, SUB>{});
+        __syncthreads();
+        read_frags<SLOT ^ 1>(0, 0);
+        mfmas(LB, NMF - Cfg::HOLD, NMF);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Fast path: the K step above with the slices it loads given by their element
+    // offsets in A and B (slice k within its tile, record-count mask v).
+    template <int SLOT, bool ENDS = false>
+    __device__ __forceinline__ void kstep_at(long long a_off, long long b_off, int k, int v, bool after_store,
+                                             int sc) {
+        static_assert(FAST, "direct-to-LDS pipeline");
+        {
+            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_off, v);
+            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_off, v);
+            if constexpr (EDGE) klim = g.K - k * BK;
             fast_sub<SLOT, 0>(ra_, rb_);
             fast_sub<SLOT, 1>(ra_, rb_);
             if constexpr (ENDS)
@@ -970,15 +987,11 @@ struct Engine {
                 barrier_after_loads<0>();
             fast_sub<SLOT, 2>(ra_, rb_);
             fast_sub<SLOT, 3>(ra_, rb_);
-            return;
         }
-        constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
-        substeps<SLOT>(nx, std::make_integer_sequence<int, SUB>{});
-        __syncthreads();
-        read_frags<SLOT ^ 1>(0, 0);
-        mfmas(LB, NMF - Cfg::HOLD, NMF);
-        __builtin_amdgcn_sched_barrier(0);
     }
+    // Element distance between consecutive slices of A (B).
+    __device__ __forceinline__ long long a_kstride() const { return AT ? (long long)BK * g.lda : BK; }
+    __device__ __forceinline__ long long b_kstride() const { return BT ? BK : (long long)BK * g.ldb; }
 
     // Fast path: the fragments of the first two sub-steps of slot SLOT, as the
     // last two sub-steps of the K step before read them.
@@ -1472,7 +1485,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     pc.stop(g);
 }
 
-// Cross-tile mode on the direct-to-LDS tiles with an even number (at least two) of
+// Cross-tile mode on the direct-to-LDS tiles with an even number (at least eight) of
 // K steps per tile: the same (tile, k) sequence as the flattened loop, run as a
 // loop over the program's tiles with the K loop inside, so that the per-step work
 // has no cursor to advance.  The loads stay two items ahead, so the last two K
@@ -1513,28 +1526,41 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
         }
     }
     e.prologue_loads(typename E::Next{m0, 0, -1, n0, 0, -1}, typename E::Next{m0, 1, -1, n0, 1, -1});
+    const long long a_ks = e.a_kstride(), b_ks = e.b_kstride();
     for (int i = 0; i < nt; ++i) {
-        const int vn = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
-        // loads of K step k: item (i, k + 2), in the next tile from k = ks - 2 on;
-        // integer masks keep the choice in scalar registers
-        auto nx = [&](int k) {
-            const int nxt = ~E::vmask(k + 2, ks);   // -1: the item is in the next tile
-            const int mm = m0 + ((m1 - m0) & nxt), nn = n0 + ((n1 - n0) & nxt);
-            const int kk = k + 2 - (ks & nxt);
-            const int vm = (vn & nxt) | ~nxt;
-            return typename E::Next{mm, kk, vm, nn, kk, vm};
+        // K step k loads item (i, k + 2), in the next tile from k = ks - 2 on (ks is
+        // even and at least 8): its slices' element offsets run on by one slice
+        // stride a step and jump to the next tile's origin after step ks - 3, so no
+        // step multiplies
+        const long long a_next = e.a_slice(m1, 0), b_next = e.b_slice(n1, 0);
+        long long a_ld = e.a_slice(m0, 2), b_ld = e.b_slice(n0, 2);
+        int kl = 2, vl = -1;   // slice index within its tile, record-count mask
+        auto advance = [&](int k) {   // after step k: the loads of step k + 1
+            if (k + 3 == ks) {
+                a_ld = a_next;
+                b_ld = b_next;
+                kl = 0;
+                vl = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
+            } else {
+                a_ld += a_ks;
+                b_ld += b_ks;
+                ++kl;
+            }
         };
         // the first slice of this tile has landed; behind it are its second slice
         // and the stores of the tile before, which may stay in flight
         e.template barrier_behind_stores<E::NLD>(sc);
         e.template reread_frags<0>();
         e.zero_acc();
-        e.template kstep<0>(nx(0), i > 0, sc);
+        e.template kstep_at<0>(a_ld, b_ld, kl, vl, i > 0, sc);
+        advance(0);
         for (int k = 1; k < ks - 1; k += 2) {
-            e.template kstep<1>(nx(k));
-            e.template kstep<0>(nx(k + 1));
+            e.template kstep_at<1>(a_ld, b_ld, kl, vl, false, 0);
+            advance(k);
+            e.template kstep_at<0>(a_ld, b_ld, kl, vl, false, 0);
+            advance(k + 1);
         }
-        e.template kstep<1, true>(nx(ks - 1));
+        e.template kstep_at<1, true>(a_ld, b_ld, kl, vl, false, 0);
         e.store_tile(m0, n0);
         sc = e.store_class(m0, n0);
         m0 = m1;
