@@ -1485,8 +1485,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     pc.stop(g);
 }
 
-// Cross-tile mode on the direct-to-LDS tiles with an even number (at least eight) of
-// K steps per tile: the same (tile, k) sequence as the flattened loop, run as a
+// Cross-tile mode on the direct-to-LDS tiles with an even number of K steps per
+// tile: the same (tile, k) sequence as the flattened loop, run as a
 // loop over the program's tiles with the K loop inside, so that the per-step work
 // has no cursor to advance.  The loads stay two items ahead, so the last two K
 // steps of a tile load the first two slices of the next one, and those are in
@@ -1529,18 +1529,19 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
     const long long a_ks = e.a_kstride(), b_ks = e.b_kstride();
     for (int i = 0; i < nt; ++i) {
         // K step k loads item (i, k + 2), in the next tile from k = ks - 2 on (ks is
-        // even and at least 8): its slices' element offsets run on by one slice
-        // stride a step and jump to the next tile's origin after step ks - 3, so no
-        // step multiplies
+        // even): its slices' element offsets run on by one slice stride a step and
+        // jump to the next tile's origin after step ks - 3, so no step multiplies
         const long long a_next = e.a_slice(m1, 0), b_next = e.b_slice(n1, 0);
-        long long a_ld = e.a_slice(m0, 2), b_ld = e.b_slice(n0, 2);
-        int kl = 2, vl = -1;   // slice index within its tile, record-count mask
+        const int vn = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
+        const bool two = ks == 2;             // step 0 already loads the next tile
+        long long a_ld = two ? a_next : e.a_slice(m0, 2), b_ld = two ? b_next : e.b_slice(n0, 2);
+        int kl = two ? 0 : 2, vl = two ? vn : -1;   // slice index within its tile, record-count mask
         auto advance = [&](int k) {   // after step k: the loads of step k + 1
             if (k + 3 == ks) {
                 a_ld = a_next;
                 b_ld = b_next;
                 kl = 0;
-                vl = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
+                vl = vn;
             } else {
                 a_ld += a_ks;
                 b_ld += b_ks;
