@@ -97,8 +97,10 @@ enum {
     TS_MODE_STREAMK = 3,
     /* chosen by the library: TS_MODE_CROSSTILE when a tile has at most 32 K
        steps (the cross-tile page finds the merged loop paying where the tile
-       boundary is a large share of the work, i.e. at small K), else
-       TS_MODE_PERSISTENT.  ts_query reports the resolved mode. */
+       boundary is a large share of the work, i.e. at small K), or an even number
+       of at least 8 on the 128x128x64 and 8-wave 256x256x64 tiles (where the
+       nested form above runs), else TS_MODE_PERSISTENT.  ts_query reports the
+       resolved mode. */
     TS_MODE_AUTO = 4
 };
 

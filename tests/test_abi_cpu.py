@@ -263,8 +263,8 @@ def test_auto_order_is_the_models_choice(M, N, K, tile, mode, P):
 
 
 @pytest.mark.parametrize("K,expect", [(128, "crosstile"), (1024, "crosstile"), (1025, "crosstile"),
-                                      (2048, "crosstile"), (2049, "persistent"), (4096, "persistent"),
-                                      (0, "crosstile")])
+                                      (2048, "crosstile"), (2049, "persistent"), (4096, "crosstile"),
+                                      (4160, "persistent"), (8192, "crosstile"), (0, "crosstile")])
 def test_auto_mode_by_k_steps(K, expect):
     q = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256, tile="256x256x64w8"))
     assert q["mode"] == {"persistent": 1, "crosstile": 2}[expect]
