@@ -79,8 +79,8 @@ enum {
     /* as PERSISTENT, but the tile loop and the K loop are one flattened loop, so
        the next tile's first K slices are fetched while the current tile is being
        stored ("(3/n) ... cross tile pipelining", merged loop).  On the 128x128x64
-       and 8-wave 256x256x64 tiles, when a tile has an even number of at least 8 K
-       steps and the direct-to-LDS pipeline runs (ts_launch_info.masked 0, 2-5),
+       and 8-wave 256x256x64 tiles, when a tile has at least 8 K steps and the
+       direct-to-LDS pipeline runs (ts_launch_info.masked 0, 2-5),
        the same (tile, k) sequence runs as a tile loop with the K loop inside and the
        next tile's first two slices loaded by the last two K steps; the wait for them
        comes after the epilogue, so that the stores just issued stay in flight. */
@@ -97,9 +97,9 @@ enum {
     TS_MODE_STREAMK = 3,
     /* chosen by the library: TS_MODE_CROSSTILE when a tile has at most 32 K
        steps (the cross-tile page finds the merged loop paying where the tile
-       boundary is a large share of the work, i.e. at small K), or an even number
-       of at least 8 on the 128x128x64 and 8-wave 256x256x64 tiles (where the
-       nested form above runs), else TS_MODE_PERSISTENT.  ts_query reports the
+       boundary is a large share of the work, i.e. at small K), or at least 8 on
+       the 128x128x64 and 8-wave 256x256x64 tiles (where the nested form above
+       runs), else TS_MODE_PERSISTENT.  ts_query reports the
        resolved mode. */
     TS_MODE_AUTO = 4
 };

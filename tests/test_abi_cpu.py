@@ -263,11 +263,16 @@ def test_auto_order_is_the_models_choice(M, N, K, tile, mode, P):
 
 
 @pytest.mark.parametrize("K,expect", [(128, "crosstile"), (1024, "crosstile"), (1025, "crosstile"),
-                                      (2048, "crosstile"), (2049, "persistent"), (4096, "crosstile"),
-                                      (4160, "persistent"), (8192, "crosstile"), (0, "crosstile")])
+                                      (2048, "crosstile"), (2049, "crosstile"), (4096, "crosstile"),
+                                      (4160, "crosstile"), (8192, "crosstile"), (0, "crosstile")])
 def test_auto_mode_by_k_steps(K, expect):
+    # the 8-wave tile: the flattened loop up to 32 K steps, the nested cross-tile
+    # kernel from 8 steps on, so cross-tile at every K
     q = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256, tile="256x256x64w8"))
     assert q["mode"] == {"persistent": 1, "crosstile": 2}[expect]
+    # the 64 x 64 tile has no nested kernel: persistent above 32 K steps
+    q = ts.query(16384, 16384, K, ts.Schedule(mode="auto", num_programs=256, tile="64x64x32"))
+    assert q["mode"] == (2 if -(-K // 32) <= 32 else 1)
     # the 4-wave 256 tile has no cross-tile kernel: auto falls back to persistent
     q = ts.query(16384, 16384, 128, ts.Schedule(mode="auto", num_programs=256, tile="256x256x64"))
     assert q["mode"] == 1

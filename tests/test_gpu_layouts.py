@@ -51,10 +51,11 @@ def test_layouts_integer_inputs_bit_exact(layout, tile, whole):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
-def test_layouts_nested_crosstile_bit_exact(layout, tile):
-    # 8 K steps per tile: the cross-tile mode runs the nested kernel on every layout
+@pytest.mark.parametrize("steps", [8, 9])
+def test_layouts_nested_crosstile_bit_exact(layout, tile, steps):
+    # 8 or 9 K steps per tile: the cross-tile mode runs the nested kernel on every layout
     bm, bn, bk = (int(v) for v in tile[:-2 if tile[-2:] in ("w8", "pp") else None].split("x"))
-    M, N, K = 2 * bm, 3 * bn, 8 * bk
+    M, N, K = 2 * bm, 3 * bn, steps * bk
     A, B = workloads.pair(M, N, K, "f16", "int", 820)
     C, _ = og.gemm(A, B, "f16")
     a, b = operands(A, B, "f16", layout)

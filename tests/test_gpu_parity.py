@@ -206,15 +206,19 @@ def test_edge_path_integer_inputs_bit_exact(tile):
 
 @pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
 @pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
-@pytest.mark.parametrize("shape", ["whole", "edges"])
-def test_nested_crosstile_integer_inputs_bit_exact(tile, ab, c_dtype, shape):
-    # cross-tile mode with 8 or 10 K steps per tile runs the nested kernel, whose last
+@pytest.mark.parametrize("shape,steps", [("whole", 8), ("edges", 10), ("whole", 9), ("edges", 11)])
+def test_nested_crosstile_integer_inputs_bit_exact(tile, ab, c_dtype, shape, steps):
+    # cross-tile mode with 8 to 11 K steps per tile runs the nested kernel, whose last
     # K step of a tile does not wait for the next slice and whose post-epilogue wait
-    # counts the stores of the tile just stored (edge tiles: none counted); one, a
-    # few and many tiles per program; exact integer products, and bit-identical to
-    # the persistent kernel
+    # counts the stores of the tile just stored (edge tiles: none counted); with an
+    # odd count consecutive tiles start on alternate slots; one, a few and many
+    # tiles per program; exact integer products, and bit-identical to the
+    # persistent kernel
     bm, bn, bk = tile_dims(tile)
-    M, N, K = (3 * bm, 5 * bn, 8 * bk) if shape == "whole" else (3 * bm + 5, 4 * bn + 8, 9 * bk + 8)
+    if shape == "whole":
+        M, N, K = 3 * bm, 5 * bn, steps * bk
+    else:
+        M, N, K = 3 * bm + 5, 4 * bn + 8, (steps - 1) * bk + 8
     A, B = workloads.pair(M, N, K, ab, "int", 640)
     C, _ = og.gemm(A, B, ab, threads=4)
     expect = round_to(C, c_dtype)

@@ -110,14 +110,13 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
 }
 
 // The nested cross-tile kernel (MODE_XTILE) runs the cross-tile mode on the 128 x
-// 128 and 8-wave 256 x 256 direct-to-LDS tiles when a tile has an even number of
-// at least this many K steps; with fewer, its epilogues come so close together
-// that the deeper queue of stores slows the loads behind them (measured on the
-// 16384^2 product: 10 % slower than the flattened loop at 2 steps, 2-3 % at 4 and
-// 6, 4 % faster at 8).
+// 128 and 8-wave 256 x 256 direct-to-LDS tiles when a tile has at least this many
+// K steps; with fewer, its epilogues come so close together that the deeper queue
+// of stores slows the loads behind them (measured on the 16384^2 product: 9-10 %
+// slower than the flattened loop at 2 steps, 2-4 % at 4 and 6, level at 8).
 constexpr int kXtileMinSteps = 8;
 bool xtile_shape(int cfg, int64_t ks) {
-    return (cfg == CFG_128 || cfg == CFG_256W8) && ks >= kXtileMinSteps && ks % 2 == 0;
+    return (cfg == CFG_128 || cfg == CFG_256W8) && ks >= kXtileMinSteps;
 }
 
 // Kernel mode of a plan: MODE_XTILE where the nested cross-tile kernel runs, else

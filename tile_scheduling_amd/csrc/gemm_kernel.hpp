@@ -1485,8 +1485,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     pc.stop(g);
 }
 
-// Cross-tile mode on the direct-to-LDS tiles with an even number of K steps per
-// tile: the same (tile, k) sequence as the flattened loop, run as a
+// Cross-tile mode on the direct-to-LDS tiles with at least two K steps per tile: the same (tile, k) sequence as the flattened loop, run as a
 // loop over the program's tiles with the K loop inside, so that the per-step work
 // has no cursor to advance.  The loads stay two items ahead, so the last two K
 // steps of a tile load the first two slices of the next one, and those are in
@@ -1527,10 +1526,14 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
     }
     e.prologue_loads(typename E::Next{m0, 0, -1, n0, 0, -1}, typename E::Next{m0, 1, -1, n0, 1, -1});
     const long long a_ks = e.a_kstride(), b_ks = e.b_kstride();
-    for (int i = 0; i < nt; ++i) {
-        // K step k loads item (i, k + 2), in the next tile from k = ks - 2 on (ks is
-        // even): its slices' element offsets run on by one slice stride a step and
-        // jump to the next tile's origin after step ks - 3, so no step multiplies
+    // one tile: S0 is the slot of its first K step (item i * ks); ODD: ks is odd,
+    // so the slots of consecutive tiles start alternately on 0 and 1
+    auto run_tile = [&](int i, auto s0_tag, auto odd_tag) {
+        constexpr int S0 = decltype(s0_tag)::value;
+        constexpr bool ODD = decltype(odd_tag)::value;
+        // K step k loads item (i, k + 2), in the next tile from k = ks - 2 on: its
+        // slices' element offsets run on by one slice stride a step and jump to the
+        // next tile's origin after step ks - 3, so no step multiplies
         const long long a_next = e.a_slice(m1, 0), b_next = e.b_slice(n1, 0);
         const int vn = E::vmask(i + 1, nt);   // -1 if there is a next tile, else 0
         const bool two = ks == 2;             // step 0 already loads the next tile
@@ -1551,17 +1554,25 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
         // the first slice of this tile has landed; behind it are its second slice
         // and the stores of the tile before, which may stay in flight
         e.template barrier_behind_stores<E::NLD>(sc);
-        e.template reread_frags<0>();
+        e.template reread_frags<S0>();
         e.zero_acc();
-        e.template kstep_at<0>(a_ld, b_ld, kl, vl, i > 0, sc);
+        e.template kstep_at<S0>(a_ld, b_ld, kl, vl, i > 0, sc);
         advance(0);
-        for (int k = 1; k < ks - 1; k += 2) {
-            e.template kstep_at<1>(a_ld, b_ld, kl, vl, false, 0);
+        // steps 1 .. ks - 2 in pairs (odd ks: the last of them alone), then the last
+        const int kend = ODD ? ks - 2 : ks - 1;
+        for (int k = 1; k < kend; k += 2) {
+            e.template kstep_at<S0 ^ 1>(a_ld, b_ld, kl, vl, false, 0);
             advance(k);
-            e.template kstep_at<0>(a_ld, b_ld, kl, vl, false, 0);
+            e.template kstep_at<S0>(a_ld, b_ld, kl, vl, false, 0);
             advance(k + 1);
         }
-        e.template kstep_at<1, true>(a_ld, b_ld, kl, vl, false, 0);
+        if constexpr (ODD) {
+            e.template kstep_at<S0 ^ 1>(a_ld, b_ld, kl, vl, false, 0);
+            advance(ks - 2);
+            e.template kstep_at<S0, true>(a_ld, b_ld, kl, vl, false, 0);
+        } else {
+            e.template kstep_at<S0 ^ 1, true>(a_ld, b_ld, kl, vl, false, 0);
+        }
         e.store_tile(m0, n0);
         sc = e.store_class(m0, n0);
         m0 = m1;
@@ -1572,6 +1583,20 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
             m1 = tm * Cfg::BM;
             n1 = tn * Cfg::BN;
         }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using Even = std::integral_constant<bool, false>;
+    using Odd = std::integral_constant<bool, true>;
+    if (ks & 1) {
+        for (int i = 0; i < nt; ++i) {
+            if (i & 1)
+                run_tile(i, C1{}, Odd{});
+            else
+                run_tile(i, C0{}, Odd{});
+        }
+    } else {
+        for (int i = 0; i < nt; ++i) run_tile(i, C0{}, Even{});
     }
     e.drain();
     pc.stop(g);

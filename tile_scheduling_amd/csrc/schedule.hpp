@@ -40,8 +40,8 @@ namespace ts {
 
 enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
 enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2, MODE_STREAMK = 3 };
-// Kernel of the cross-tile mode on direct-to-LDS tiles with an even number of K
-// steps: the same (tile, k) sequence as MODE_CROSSTILE (not a schedule of its own).
+// Kernel of the cross-tile mode on direct-to-LDS tiles of at least 8 K steps: the
+// same (tile, k) sequence as MODE_CROSSTILE (not a schedule of its own).
 enum : int { MODE_XTILE = 4 };
 
 // Division by an invariant divisor d >= 1 with one multiply-high, one add and one
