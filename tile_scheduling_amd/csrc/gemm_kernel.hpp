@@ -946,18 +946,13 @@ struct Engine {
     }
 
     // `after_store`: the epilogue stores of the tile before were issued after the
-    // loads this barrier waits for; they may stay in flight.  Not on the edge paths:
-    // their masked epilogue issues a varying number of stores, so they wait for all.
-    // ENDS (fast path): the last K step of a tile whose epilogue follows, in a loop
-    // that reads the next slice's first fragments again after the epilogue; its
-    // barrier then only has to certify that every wave has finished reading this
-    // slot, and the wait for the next slice moves behind the epilogue.
-    // `sc`: store class of the tile before (store_class), default the unmasked
-    // count (edge path: none counted).
-    template <int SLOT, bool ENDS = false>
+    // loads this barrier waits for; those of store class `sc` (store_class) may
+    // stay in flight.  The default counts the unmasked epilogue's stores, and none
+    // on the edge path, whose masked epilogue issues a varying number.
+    template <int SLOT>
     __device__ __forceinline__ void kstep(const Next& nx, bool after_store = false, int sc = EDGE ? 0 : 1) {
         if constexpr (FAST) {
-            kstep_at<SLOT, ENDS>(a_slice(nx.m0, nx.ka), b_slice(nx.n0, nx.kb), nx.ka, nx.va, after_store, sc);
+            kstep_at<SLOT>(a_slice(nx.m0, nx.ka), b_slice(nx.n0, nx.kb), nx.ka, nx.va, after_store, sc);
             return;
         }
         constexpr int LB = (SUB - 1) & 1;  // fragment buffer of the last sub-step
@@ -969,25 +964,27 @@ struct Engine {
     }
     // Fast path: the K step above with the slices it loads given by their element
     // offsets in A and B (slice k within its tile, record-count mask v).
+    // ENDS: the last K step of a tile whose epilogue follows, in a loop that reads
+    // the next slice's first fragments again after the epilogue; its barrier then
+    // only has to certify that every wave has finished reading this slot, and the
+    // wait for the next slice moves behind the epilogue.
     template <int SLOT, bool ENDS = false>
     __device__ __forceinline__ void kstep_at(long long a_off, long long b_off, int k, int v, bool after_store,
                                              int sc) {
         static_assert(FAST, "direct-to-LDS pipeline");
-        {
-            const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_off, v);
-            const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_off, v);
-            if constexpr (EDGE) klim = g.K - k * BK;
-            fast_sub<SLOT, 0>(ra_, rb_);
-            fast_sub<SLOT, 1>(ra_, rb_);
-            if constexpr (ENDS)
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else if (after_store)
-                barrier_behind_stores<0>(sc);
-            else
-                barrier_after_loads<0>();
-            fast_sub<SLOT, 2>(ra_, rb_);
-            fast_sub<SLOT, 3>(ra_, rb_);
-        }
+        const __amdgpu_buffer_rsrc_t rb_ = rsrc_b(b_off, v);
+        const __amdgpu_buffer_rsrc_t ra_ = rsrc_a(a_off, v);
+        if constexpr (EDGE) klim = g.K - k * BK;
+        fast_sub<SLOT, 0>(ra_, rb_);
+        fast_sub<SLOT, 1>(ra_, rb_);
+        if constexpr (ENDS)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (after_store)
+            barrier_behind_stores<0>(sc);
+        else
+            barrier_after_loads<0>();
+        fast_sub<SLOT, 2>(ra_, rb_);
+        fast_sub<SLOT, 3>(ra_, rb_);
     }
     // Element distance between consecutive slices of A (B).
     __device__ __forceinline__ long long a_kstride() const { return AT ? (long long)BK * g.lda : BK; }
@@ -1485,9 +1482,10 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
     pc.stop(g);
 }
 
-// Cross-tile mode on the direct-to-LDS tiles with at least two K steps per tile: the same (tile, k) sequence as the flattened loop, run as a
-// loop over the program's tiles with the K loop inside, so that the per-step work
-// has no cursor to advance.  The loads stay two items ahead, so the last two K
+// Cross-tile mode on the direct-to-LDS tiles with at least two K steps per tile:
+// the same (tile, k) sequence as the flattened loop, run as a loop over the
+// program's tiles with the K loop inside, so that the per-step work has no cursor
+// to advance.  The loads stay two items ahead, so the last two K
 // steps of a tile load the first two slices of the next one, and those are in
 // flight while the tile is stored.  The last K step of a tile does not wait for
 // the next slice at its barrier (the fragments it reads ahead are read again);
