@@ -150,6 +150,28 @@ def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
     assert waves_per_simd * (q["arch_vgprs"] + q["agprs"]) <= 512
 
 
+@pytest.mark.parametrize("K,nested", [(128, False), (448, False), (512, True), (576, True), (4096, True),
+                                      (4160, True)])
+def test_crosstile_kernel_choice_by_k_steps(K, nested):
+    # the cross-tile mode on the 8-wave tile runs the nested cross-tile kernel from 8
+    # K steps per tile on (any parity), the flattened loop below; the resource report
+    # follows the kernel that runs: the nested one spills no registers
+    s = ts.Schedule(order="grouped", group_m=8, xcd_remap=True, mode="crosstile", num_programs=256,
+                    tile="256x256x64w8")
+    q = ts.query(16384, 16384, K, s)
+    ref = ts.query(16384, 16384, 512, s)   # 8 K steps: the nested kernel
+    assert q["mode"] == 2
+    report = lambda x: (x["arch_vgprs"], x["spilled_vgprs"], x["sgprs"], x["spilled_sgprs"])
+    if nested:
+        assert q["spilled_vgprs"] == 0 and report(q) == report(ref), q
+    else:
+        assert report(q) != report(ref), q   # another kernel (the flattened loop)
+    # the automatic schedule of the headline shape resolves to the nested kernel
+    if K == 4096:
+        qa = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256))
+        assert qa["mode"] == 2 and qa["spilled_vgprs"] == 0
+
+
 # ---- host-side schedule (the same functions the kernels run) vs the oracle ----------
 
 def _oracle_sched(s: ts.Schedule, grid_programs):
