@@ -70,6 +70,43 @@ def test_layouts_nested_crosstile_bit_exact(layout, tile, steps):
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
+@pytest.mark.parametrize("steps", [8, 9])
+def test_nested_crosstile_padded_strides_with_canaries(layout, tile, steps):
+    # the nested cross-tile kernel runs its slice offsets on by one row-stride-sized
+    # step a K step: padded row strides of A, B and C (the operands inside larger
+    # buffers, 16-byte aligned), exact integer products, and nothing written
+    # outside C
+    bm, bn, bk = (int(v) for v in tile[:-2 if tile[-2:] in ("w8", "pp") else None].split("x"))
+    M, N, K = 2 * bm, 3 * bn, steps * bk
+    A, B = workloads.pair(M, N, K, "f16", "int", 830)
+    C, _ = og.gemm(A, B, "f16")
+    pad = 24
+    def padded(X, transposed):
+        rows, cols = (X.shape[1], X.shape[0]) if transposed else X.shape
+        buf = torch.zeros((rows, cols + pad), dtype=torch.float16, device="cuda")
+        view = buf[:, :cols]
+        view.copy_(to_device(np.ascontiguousarray(X.T) if transposed else X, "f16"))
+        return view.t() if transposed else view
+    a, b = padded(A, layout[0] == "T"), padded(B, layout[1] == "T")
+    assert max(a.stride()) > (K if layout[0] == "N" else M) and max(b.stride()) > (N if layout[1] == "N" else K)
+    assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == 0
+    cbuf = torch.full((M + 4, N + 2 * pad), -12345.0, device="cuda")
+    c = cbuf[2:2 + M, pad:pad + N]
+    for P in (1, 4):
+        c.fill_(float("nan"))
+        s = ts.Schedule(order="grouped", group_m=2, mode="crosstile", num_programs=P, tile=tile)
+        say(f"padded {layout} {M}x{N}x{K} {s.label()}")
+        ts.gemm(a, b, out=c, schedule=s)
+        torch.cuda.synchronize()
+        bad = np.argwhere(to_f64(c) != C)
+        assert bad.size == 0, f"{layout} P={P}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+        guard = cbuf.clone()
+        guard[2:2 + M, pad:pad + N] = -12345.0
+        assert (guard == -12345.0).all(), "write outside C"
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("bf16", "f32"), ("bf16", "bf16")])
 def test_layouts_random_inputs_within_bound(layout, ab, c_dtype):
     M, N, K = 700, 900, 333
