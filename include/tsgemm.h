@@ -64,8 +64,11 @@ enum {
        G=8+remap, G=4+remap, G=16+remap, row-major, row-major+remap, G=8, G=4,
        G=16, G=2+remap, G=32+remap, G=2, G=32.  The grouping page's closing
        section says the best order depends on the size and the cache; this is
-       that choice made from a model rather than a sweep.  ts_query reports the
-       resolved order, G and remap. */
+       that choice made from a model rather than a sweep.  The model counts operand
+       reuse only: at a few K steps per tile, where writing C is most of the traffic,
+       the fastest order varies with C's row pitch and the number of tile rows, and
+       an explicit order can be faster.  ts_query reports the resolved order, G and
+       remap. */
     TS_ORDER_AUTO = 2
 };
 
