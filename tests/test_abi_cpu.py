@@ -150,22 +150,26 @@ def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
     assert waves_per_simd * (q["arch_vgprs"] + q["agprs"]) <= 512
 
 
-@pytest.mark.parametrize("K,nested", [(128, False), (448, False), (512, True), (576, True), (4096, True),
-                                      (4160, True)])
-def test_crosstile_kernel_choice_by_k_steps(K, nested):
-    # the cross-tile mode on the 8-wave tile runs the nested cross-tile kernel from 8
-    # K steps per tile on (any parity), the flattened loop below; the resource report
-    # follows the kernel that runs: the nested one spills no registers
+@pytest.mark.parametrize("M,K,kind", [(16384, 64, "flat"), (16384, 128, "plain"), (16384, 192, "plain"),
+                                      (16384, 448, "plain"), (4096, 256, "flat"), (16384, 512, "nested"),
+                                      (16384, 576, "nested"), (16384, 4096, "nested"), (16384, 4160, "nested")])
+def test_crosstile_kernel_choice_by_k_steps(M, K, kind):
+    # the cross-tile mode on the 8-wave tile runs the nested kernel with the deferred
+    # wait from 8 K steps per tile on (any parity), the nested kernel without it from
+    # 2 to 7 when a program has more than one tile, and the flattened loop otherwise
+    # (one K step; 4096^2 on 256 programs: one tile each); the resource report follows
+    # the kernel that runs, and the nested kernels spill no vector registers
     s = ts.Schedule(order="grouped", group_m=8, xcd_remap=True, mode="crosstile", num_programs=256,
                     tile="256x256x64w8")
-    q = ts.query(16384, 16384, K, s)
-    ref = ts.query(16384, 16384, 512, s)   # 8 K steps: the nested kernel
-    assert q["mode"] == 2
     report = lambda x: (x["arch_vgprs"], x["spilled_vgprs"], x["sgprs"], x["spilled_sgprs"])
-    if nested:
-        assert q["spilled_vgprs"] == 0 and report(q) == report(ref), q
-    else:
-        assert report(q) != report(ref), q   # another kernel (the flattened loop)
+    ref = {"nested": ts.query(16384, 16384, 512, s), "plain": ts.query(16384, 16384, 128, s),
+           "flat": ts.query(16384, 16384, 64, s)}
+    assert len({report(r) for r in ref.values()}) == 3, ref   # three kernels, told apart by their reports
+    q = ts.query(M, M, K, s)
+    assert q["mode"] == 2
+    assert report(q) == report(ref[kind]), (kind, q)
+    if kind != "flat":
+        assert q["spilled_vgprs"] == 0, q
     # the automatic schedule of the headline shape resolves to the nested kernel
     if K == 4096:
         qa = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256))

@@ -1502,7 +1502,13 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
 // loads it waits for, may stay in flight: a wave then waits only for the stores
 // of the tile before, one tile earlier, instead of those it has just issued
 // (loads and stores retire in issue order on one counter).
-template <class Cfg, class TI, class TO, int PATH>
+// DEFER false (tiles of 2 to 7 K steps): the last K step of a tile waits for the
+// next slice at its own barrier, as in the flattened loop, and after the epilogue
+// the next tile only reads its first fragments again, with no barrier: two barriers
+// a tile instead of three, and with the fragments read after the epilogue nothing
+// but the accumulators is live through it, so the loop needs no spills (the
+// flattened loop spills at these step counts).
+template <class Cfg, class TI, class TO, int PATH, bool DEFER = true>
 __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];
     __shared__ __attribute__((aligned(16))) char lds_b0[Cfg::B_SLOT], lds_b1[Cfg::B_SLOT];
@@ -1531,7 +1537,13 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
             n1 = tn * Cfg::BN;
         }
     }
+    // two K steps a tile: the staggered start of the flattened loop (see there)
+    if (!DEFER && ks == 2 && nt >= 8) {
+        const int grp = (blockIdx.x >> 3) & 7;
+        for (int i = 0; i < grp; ++i) __builtin_amdgcn_s_sleep(32);
+    }
     e.prologue_loads(typename E::Next{m0, 0, -1, n0, 0, -1}, typename E::Next{m0, 1, -1, n0, 1, -1});
+    if constexpr (!DEFER) e.template barrier_after_loads<E::NLD>();   // the first slice has landed
     const long long a_ks = e.a_kstride(), b_ks = e.b_kstride();
     // one tile: S0 is the slot of its first K step (item i * ks); ODD: ks is odd,
     // so the slots of consecutive tiles start alternately on 0 and 1
@@ -1559,8 +1571,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
             }
         };
         // the first slice of this tile has landed; behind it are its second slice
-        // and the stores of the tile before, which may stay in flight
-        e.template barrier_behind_stores<E::NLD>(sc);
+        // and the stores of the tile before, which may stay in flight (DEFER false:
+        // the last K step's barrier or the prologue has already waited for it)
+        if constexpr (DEFER) e.template barrier_behind_stores<E::NLD>(sc);
         e.template reread_frags<S0>();
         e.zero_acc();
         e.template kstep_at<S0>(a_ld, b_ld, kl, vl, i > 0, sc);
@@ -1576,9 +1589,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
         if constexpr (ODD) {
             e.template kstep_at<S0 ^ 1>(a_ld, b_ld, kl, vl, false, 0);
             advance(ks - 2);
-            e.template kstep_at<S0, true>(a_ld, b_ld, kl, vl, false, 0);
+            e.template kstep_at<S0, DEFER>(a_ld, b_ld, kl, vl, false, 0);
         } else {
-            e.template kstep_at<S0 ^ 1, true>(a_ld, b_ld, kl, vl, false, 0);
+            e.template kstep_at<S0 ^ 1, DEFER>(a_ld, b_ld, kl, vl, false, 0);
         }
         e.store_tile(m0, n0);
         sc = e.store_class(m0, n0);

@@ -44,6 +44,11 @@ const void* kernel_by_mode(int mode) {
                 return reinterpret_cast<const void*>(&gemm_xtile_kernel<Cfg, TI, TO, PATH>);
             else
                 return nullptr;
+        case MODE_XTILE_PLAIN:
+            if constexpr (has_flat_kernel<Cfg>() && Engine<Cfg, TI, TO, PATH>::FAST)
+                return reinterpret_cast<const void*>(&gemm_xtile_kernel<Cfg, TI, TO, PATH, false>);
+            else
+                return nullptr;
         default:
             if constexpr (has_flat_kernel<Cfg>())
                 return reinterpret_cast<const void*>(&gemm_flat_kernel<Cfg, TI, TO, PATH>);

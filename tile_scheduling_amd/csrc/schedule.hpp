@@ -40,9 +40,10 @@ namespace ts {
 
 enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
 enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2, MODE_STREAMK = 3 };
-// Kernel of the cross-tile mode on direct-to-LDS tiles of at least 8 K steps: the
-// same (tile, k) sequence as MODE_CROSSTILE (not a schedule of its own).
-enum : int { MODE_XTILE = 4 };
+// Kernels of the cross-tile mode on direct-to-LDS tiles, the same (tile, k)
+// sequence as MODE_CROSSTILE (not schedules of their own): the nested loop with
+// the deferred wait (at least 8 K steps) and without it (2 to 7).
+enum : int { MODE_XTILE = 4, MODE_XTILE_PLAIN = 5 };
 
 // Division by an invariant divisor d >= 1 with one multiply-high, one add and one
 // shift, after Granlund and Montgomery, "Division by invariant integers using
