@@ -83,11 +83,10 @@ enum {
        the next tile's first K slices are fetched while the current tile is being
        stored ("(3/n) ... cross tile pipelining", merged loop).  On the 128x128x64
        and 8-wave 256x256x64 tiles, when the direct-to-LDS pipeline runs
-       (ts_launch_info.masked 0, 2-5) and a tile has at least 8 K steps, or 2 to 7
-       with more than one tile per program, the same (tile, k) sequence runs as a
-       tile loop with the K loop inside and the next tile's first two slices loaded
-       by the last two K steps; from 8 K steps on, the wait for them comes after the
-       epilogue, so that the stores just issued stay in flight. */
+       (ts_launch_info.masked 0, 2-5) and a tile has at least 2 K steps (with one
+       tile per program: at least 8), the same (tile, k) sequence runs as a tile
+       loop with the K loop inside and the next tile's first two slices loaded by
+       the last two K steps. */
     TS_MODE_CROSSTILE = 2,
     /* stream-K, the follow-on the persistent page names for its tail (the split is
        this library's design): the first num_tiles - (num_tiles mod P) tiles run as

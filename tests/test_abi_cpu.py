@@ -151,18 +151,20 @@ def test_query_reports_the_compilers_resource_use(tile, M, N, K, mode):
 
 
 @pytest.mark.parametrize("M,K,kind", [(16384, 64, "flat"), (16384, 128, "plain"), (16384, 192, "plain"),
-                                      (16384, 448, "plain"), (4096, 256, "flat"), (16384, 512, "nested"),
-                                      (16384, 576, "nested"), (16384, 4096, "nested"), (16384, 4160, "nested")])
+                                      (16384, 448, "plain"), (16384, 512, "plain"), (16384, 576, "plain"),
+                                      (16384, 4096, "plain"), (16384, 4160, "plain"), (4096, 256, "flat"),
+                                      (4096, 512, "deferred"), (4096, 4096, "deferred")])
 def test_crosstile_kernel_choice_by_k_steps(M, K, kind):
-    # the cross-tile mode on the 8-wave tile runs the nested kernel with the deferred
-    # wait from 8 K steps per tile on (any parity), the nested kernel without it from
-    # 2 to 7 when a program has more than one tile, and the flattened loop otherwise
-    # (one K step; 4096^2 on 256 programs: one tile each); the resource report follows
-    # the kernel that runs, and the nested kernels spill no vector registers
+    # the cross-tile mode on the 8-wave tile runs the nested kernel without the
+    # deferred wait when a program has more than one tile (16384^2 on 256 programs:
+    # 16) and at least 2 K steps; with one tile per program (4096^2: 256 tiles) the
+    # nested kernel with the deferred wait from 8 K steps on; the flattened loop
+    # otherwise (one K step; one tile of 2 to 7).  The resource report follows the
+    # kernel that runs, and the nested kernels spill no vector registers.
     s = ts.Schedule(order="grouped", group_m=8, xcd_remap=True, mode="crosstile", num_programs=256,
                     tile="256x256x64w8")
     report = lambda x: (x["arch_vgprs"], x["spilled_vgprs"], x["sgprs"], x["spilled_sgprs"])
-    ref = {"nested": ts.query(16384, 16384, 512, s), "plain": ts.query(16384, 16384, 128, s),
+    ref = {"plain": ts.query(16384, 16384, 512, s), "deferred": ts.query(4096, 4096, 4096, s),
            "flat": ts.query(16384, 16384, 64, s)}
     assert len({report(r) for r in ref.values()}) == 3, ref   # three kernels, told apart by their reports
     q = ts.query(M, M, K, s)
@@ -170,10 +172,10 @@ def test_crosstile_kernel_choice_by_k_steps(M, K, kind):
     assert report(q) == report(ref[kind]), (kind, q)
     if kind != "flat":
         assert q["spilled_vgprs"] == 0, q
-    # the automatic schedule of the headline shape resolves to the nested kernel
-    if K == 4096:
+    # the automatic schedule of the headline shape resolves to a nested kernel
+    if K == 4096 and M == 16384:
         qa = ts.query(16384, 16384, K, ts.Schedule(order="auto", mode="auto", num_programs=256))
-        assert qa["mode"] == 2 and qa["spilled_vgprs"] == 0
+        assert qa["mode"] == 2 and report(qa) == report(ref["plain"])
 
 
 # ---- host-side schedule (the same functions the kernels run) vs the oracle ----------

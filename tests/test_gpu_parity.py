@@ -202,17 +202,19 @@ def test_edge_path_integer_inputs_bit_exact(tile):
             assert np.array_equal(got, C), (M, N, K, mode)
 
 
-# ---- the nested cross-tile kernel (an even number of at least 8 K steps) -----------
+# ---- the nested cross-tile kernels (at least 8 K steps) ------------------------------
 
 @pytest.mark.parametrize("tile", ["128x128x64", "256x256x64w8"])
 @pytest.mark.parametrize("ab,c_dtype", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 @pytest.mark.parametrize("shape,steps", [("whole", 8), ("edges", 10), ("whole", 9), ("edges", 11)])
 def test_nested_crosstile_integer_inputs_bit_exact(tile, ab, c_dtype, shape, steps):
-    # cross-tile mode with 8 to 11 K steps per tile runs the nested kernel, whose last
-    # K step of a tile does not wait for the next slice and whose post-epilogue wait
-    # counts the stores of the tile just stored (edge tiles: none counted); with an
-    # odd count consecutive tiles start on alternate slots; one, a few and many
-    # tiles per program; exact integer products, and bit-identical to the
+    # cross-tile mode with 8 to 11 K steps per tile runs a nested kernel: where a
+    # program has more than one tile (P = 1 and 4; 15 on the 20 edge-shape tiles)
+    # the one without the deferred wait, where each has one (P = 15 on the 15
+    # whole-shape tiles, P = 32) the one whose last K step of a tile does not wait
+    # for the next slice and whose post-epilogue wait counts the stores of the tile
+    # just stored (edge tiles: none counted); with an odd count consecutive tiles
+    # start on alternate slots; exact integer products, and bit-identical to the
     # persistent kernel
     bm, bn, bk = tile_dims(tile)
     if shape == "whole":
@@ -223,7 +225,7 @@ def test_nested_crosstile_integer_inputs_bit_exact(tile, ab, c_dtype, shape, ste
     C, _ = og.gemm(A, B, ab, threads=4)
     expect = round_to(C, c_dtype)
     assert ts.query(M, N, K, ts.Schedule(tile=tile))["masked"] == (0 if shape == "whole" else 2)
-    for P in (1, 4, 15):
+    for P in (1, 4, 15, 32):
         outs = []
         for mode in ("crosstile", "persistent"):
             s = ts.Schedule(order="grouped", group_m=2, mode=mode, num_programs=P, xcd_remap=True, tile=tile)

@@ -109,34 +109,39 @@ void cfg_dims(int cfg, int* bm, int* bn, int* bk) {
     }
 }
 
-// The nested cross-tile kernel (MODE_XTILE) runs the cross-tile mode on the 128 x
-// 128 and 8-wave 256 x 256 direct-to-LDS tiles when a tile has at least this many
-// K steps; with fewer, its epilogues come so close together that the deeper queue
-// of stores slows the loads behind them (measured on the 16384^2 product: 9-10 %
-// slower than the flattened loop at 2 steps, 2-4 % at 4 and 6, level at 8).
+// The nested cross-tile kernels run on the 128 x 128 and 8-wave 256 x 256
+// direct-to-LDS tiles.  The one with the deferred wait (MODE_XTILE) needs at least
+// this many K steps a tile: with fewer, its epilogues come so close together that
+// the deeper queue of stores slows the loads behind them (measured on the 16384^2
+// product: 9-10 % slower than the flattened loop at 2 steps, 2-4 % at 4 and 6,
+// level at 8); it runs where a program has one tile (below).  TS_MODE_AUTO takes
+// the cross-tile mode wherever a tile has at least this many steps on these tiles.
 constexpr int kXtileMinSteps = 8;
 bool xtile_shape(int cfg, int64_t ks) {
     return (cfg == CFG_128 || cfg == CFG_256W8) && ks >= kXtileMinSteps;
 }
 
 // The nested kernel without the deferred wait (MODE_XTILE_PLAIN) runs the
-// cross-tile mode on the same tiles from 2 to 7 K steps when a program has more
-// than one tile (before the grid is resolved: always): two barriers a tile as in
-// the flattened loop, but no spills where the flattened loop spills (measured on
-// the 16384^2 product, interleaved: fp32 output 21 % faster at K = 128 and 11 % at
-// K = 256 with bf16 inputs, fp16 3 % at K = 128 and 256, level from 5 to 7 steps,
-// 2.5 % slower at 3; with one tile per program, 4096^2 at K = 256, 6 % slower).
+// cross-tile mode on the same tiles from 2 K steps on when a program has more than
+// one tile (before the grid is resolved: always): two barriers a tile as in the
+// flattened loop, but no spills where the flattened loop spills.  Measured on the
+// 16384^2 product, interleaved: against the flattened loop, fp32 output 21 % faster
+// at K = 128 and 11 % at K = 256 with bf16 inputs, fp16 3 % at K = 128 and 256,
+// level from 5 to 7 steps, 2.5 % slower at 3; against the nested kernel with the
+// deferred wait, 2.6 % faster at K = 512, 1.4 % at 1024, 0.3 % at 4096 and 1-1.5 %
+// on the 5000 x 12290 x 1000 product.  With one tile per program there is no tile
+// boundary to overlap: the flattened loop runs below 8 K steps (4096^2 at K = 256:
+// 6 % faster than this kernel) and the deferred-wait kernel from 8 on.
 bool xtile_plain_shape(const Plan& p) {
-    return (p.cfg == CFG_128 || p.cfg == CFG_256W8) && p.s.ks >= 2 && p.s.ks < kXtileMinSteps &&
-           (p.s.grid <= 0 || p.s.num_tiles > p.s.grid);
+    return (p.cfg == CFG_128 || p.cfg == CFG_256W8) && p.s.ks >= 2 && (p.s.grid <= 0 || p.s.num_tiles > p.s.grid);
 }
 
-// Kernel mode of a plan: MODE_XTILE or MODE_XTILE_PLAIN where a nested cross-tile
+// Kernel mode of a plan: MODE_XTILE_PLAIN or MODE_XTILE where a nested cross-tile
 // kernel runs, else the plan's own mode.
 int kernel_mode(const Plan& p) {
     if (p.mode == TS_MODE_CROSSTILE && p.path != PATH_MASKED) {
-        if (xtile_shape(p.cfg, p.s.ks)) return MODE_XTILE;
         if (xtile_plain_shape(p)) return MODE_XTILE_PLAIN;
+        if (xtile_shape(p.cfg, p.s.ks)) return MODE_XTILE;
     }
     return p.mode;
 }

@@ -1502,12 +1502,12 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_flat_kernel(GemmArgs g) {
 // loads it waits for, may stay in flight: a wave then waits only for the stores
 // of the tile before, one tile earlier, instead of those it has just issued
 // (loads and stores retire in issue order on one counter).
-// DEFER false (tiles of 2 to 7 K steps): the last K step of a tile waits for the
-// next slice at its own barrier, as in the flattened loop, and after the epilogue
-// the next tile only reads its first fragments again, with no barrier: two barriers
-// a tile instead of three, and with the fragments read after the epilogue nothing
-// but the accumulators is live through it, so the loop needs no spills (the
-// flattened loop spills at these step counts).
+// DEFER false (programs of more than one tile): the last K step of a tile waits for
+// the next slice at its own barrier, as in the flattened loop, and after the
+// epilogue the next tile only reads its first fragments again, with no barrier: two
+// barriers a tile instead of three, and with the fragments read after the epilogue
+// nothing but the accumulators is live through it, so the loop needs no spills (the
+// flattened loop spills).
 template <class Cfg, class TI, class TO, int PATH, bool DEFER = true>
 __global__ void __launch_bounds__(Cfg::NT) gemm_xtile_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) char lds_a0[Cfg::A_SLOT], lds_a1[Cfg::A_SLOT];

@@ -41,8 +41,9 @@ namespace ts {
 enum : int { ORDER_ROW_MAJOR = 0, ORDER_GROUPED = 1 };
 enum : int { MODE_TILED = 0, MODE_PERSISTENT = 1, MODE_CROSSTILE = 2, MODE_STREAMK = 3 };
 // Kernels of the cross-tile mode on direct-to-LDS tiles, the same (tile, k)
-// sequence as MODE_CROSSTILE (not schedules of their own): the nested loop with
-// the deferred wait (at least 8 K steps) and without it (2 to 7).
+// sequence as MODE_CROSSTILE (not schedules of their own): the nested loop with the
+// deferred wait (one tile per program, at least 8 K steps) and without it (programs
+// of more than one tile, at least 2 K steps).
 enum : int { MODE_XTILE = 4, MODE_XTILE_PLAIN = 5 };
 
 // Division by an invariant divisor d >= 1 with one multiply-high, one add and one
